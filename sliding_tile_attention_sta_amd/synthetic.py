@@ -1,0 +1,125 @@
+"""Seeded synthetic STA workloads: shapes, windows and value distributions.
+
+This module holds no attention arithmetic.  It only draws inputs, and it is
+the one module that both the HIP path's callers (tests, bench, smoke) and
+the CPU oracle's callers share.  The video shape (30, 48, 80) of the larger
+workloads is the 720p, 5-second latent named on the gptget summary page
+("Experiments"); there are no real activations here, so Q, K and V are
+N(0, 1) draws of that shape instead.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "sample_query_tiles", "tile_count"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int                      # seed = 1000 * index
+    video: tuple                    # (T, H, W) tokens
+    tile: tuple                     # (tT, tH, tW) tokens
+    windows: tuple                  # one (wT, wH, wW) per head, in tiles
+    head_dim: int
+    dtype: str                      # "f32" or "bf16": dtype of Q, K, V
+    batch: int = 1
+    magnitude: tuple | None = None  # per-token magnitude range (lo, hi)
+    description: str = field(default="", compare=False)
+
+    @property
+    def heads(self) -> int:
+        return len(self.windows)
+
+    @property
+    def seed(self) -> int:
+        return 1000 * self.index
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def tokens(self) -> int:
+        return self.video[0] * self.video[1] * self.video[2]
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def with_heads(self, heads: int) -> "Workload":
+        ws = tuple(self.windows[h % len(self.windows)] for h in range(heads))
+        return Workload(self.name, self.index, self.video, self.tile, ws, self.head_dim,
+                        self.dtype, self.batch, self.magnitude, self.description)
+
+
+_MIXED = ((1, 1, 1), (3, 3, 3), (3, 5, 5), (5, 6, 10))
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, (6, 16, 16), (2, 4, 4), ((3, 3, 3),) * 2, 64, "f32",
+                     description="6x16x16 latent, tile 2x4x4, window 3x3x3, 2 heads, d64, fp32"),
+    "small": Workload("small", 2, (12, 24, 24), (6, 8, 8), ((3, 3, 3),) * 8, 128, "bf16",
+                      description="12x24x24 latent, tile 6x8x8, window 3x3x3 (covers the grid), "
+                                  "8 heads, d128, bf16"),
+    "720p": Workload("720p", 3, (30, 48, 80), (6, 8, 8), ((3, 3, 3),) * 24, 128, "bf16",
+                     description="30x48x80 latent (115200 tokens), tile 6x8x8, window 3x3x3, "
+                                 "24 heads, d128, bf16"),
+    "mixed": Workload("mixed", 4, (30, 48, 80), (6, 8, 8),
+                      tuple(_MIXED[h % 4] for h in range(24)), 128, "bf16",
+                      description="30x48x80 latent, tile 6x8x8, 24 heads with windows cycling "
+                                  "1x1x1, 3x3x3, 3x5x5, 5x6x10, d128, bf16"),
+    "long": Workload("long", 5, (60, 48, 80), (6, 8, 8), ((3, 3, 3),) * 24, 128, "bf16",
+                     magnitude=(0.5, 4.0),
+                     description="60x48x80 latent (230400 tokens), tile 6x8x8, window 3x3x3, "
+                                 "24 heads, d128, bf16, per-token magnitude U(0.5, 4)"),
+}
+
+
+def tile_count(w: Workload) -> tuple[int, int, int]:
+    return tuple(e // t for e, t in zip(w.video, w.tile))
+
+
+def make_qkv(w: Workload, device: str | torch.device = "cpu"):
+    """Q, K, V in natural layout [B, heads, T, H, W, D], drawn from one
+    generator seeded with 1000 * index on ``device``: Q, K, V ~ N(0, 1) in
+    that order, then (if the workload has one) a per-token magnitude
+    m ~ U(lo, hi) of shape [B, T, H, W] for each of Q, K, V, shared across
+    heads and channels.  Finally cast (round to nearest even) to the
+    workload's dtype.  Values depend on the device's generator; callers pass
+    the very same tensors to both sides of a comparison."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    T, H, W = w.video
+    shape = (w.batch, w.heads, T, H, W, w.head_dim)
+    out = []
+    for _ in range(3):
+        out.append(torch.randn(shape, generator=g, device=dev, dtype=torch.float32))
+    if w.magnitude is not None:
+        lo, hi = w.magnitude
+        for i in range(3):
+            m = torch.empty((w.batch, 1, T, H, W, 1), device=dev, dtype=torch.float32)
+            m.uniform_(lo, hi, generator=g)
+            out[i].mul_(m)
+    return tuple(x.to(w.torch_dtype) for x in out)
+
+
+def sample_query_tiles(w: Workload, head: int, count: int = 64) -> list[tuple[int, int, int]]:
+    """Query tiles checked for one head on large workloads: ``count`` tiles
+    from a permutation seeded with 1000 * index + 1 + head, plus the 8 corner
+    tiles of the grid (where windows are shifted inward)."""
+    nT, nH, nW = tile_count(w)
+    n = nT * nH * nW
+    g = torch.Generator()
+    g.manual_seed(w.seed + 1 + head)
+    picks = torch.randperm(n, generator=g)[:min(count, n)].tolist()
+    tiles = {(p // (nH * nW), (p // nW) % nH, p % nW) for p in picks}
+    for a in (0, nT - 1):
+        for b in (0, nH - 1):
+            for c in (0, nW - 1):
+                tiles.add((a, b, c))
+    return sorted(tiles)
