@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the STA forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p]
+
+One step is one pass of the whole hot path over one batch of synthetic
+input: the STA forward over Q, K, V in natural [B, heads, T, H, W, D] order
+(the tile-major permutation is applied inside the kernel through its row
+tables) producing O in the same order.  Inputs are resident in HBM before
+the timed region.  Printed: one JSON line with the achieved TFLOP/s
+(FLOPs of the attended tile pairs only), the forward kernel's roofline
+position, and the CPU oracle timed on a bounded sample of the same workload.
+Context lines (not the metric): the explicit reorder -> tile-major forward ->
+unreorder path, and the same kernel with a full window (dense attention).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "STA fwd ms + achieved TFLOP/s (MFMA util) at 30×48×80 tok, 24h, d128 bf16"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 (and fp16) MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="720p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "profiles", "traffic.json"))
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(w, q, k, v, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample: query tiles of head 0
+    (then 1, ...) until about budget_s seconds of CPU work."""
+    import numpy as np
+    from oracle import sta_oracle as O
+    from sliding_tile_attention_sta_amd.synthetic import sample_query_tiles
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    grid = O.tile_grid(w.video, w.tile)
+    V = w.tile[0] * w.tile[1] * w.tile[2]
+    done_tiles, flops, t_used = 0, 0.0, 0.0
+    h = 0
+    while t_used < budget_s and h < w.heads:
+        qh, kh, vh = (x[:, h:h + 1].float().cpu().numpy() for x in (q, k, v))
+        we = O.effective_window(w.windows[h], grid)
+        for c in sample_query_tiles(w, h):
+            t0 = time.perf_counter()
+            O.sta_forward_query_tiles(qh, kh, vh, w.tile, w.windows[h], 0, [c], scale=w.scale)
+            t_used += time.perf_counter() - t0
+            done_tiles += 1
+            flops += 4.0 * V * V * w.head_dim * we[0] * we[1] * we[2]
+            if t_used >= budget_s:
+                break
+        h += 1
+    full_s = t_used * O.sta_flops(w.video, w.tile, w.windows, w.head_dim, w.batch) / flops
+    return {
+        "value": flops / t_used / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done_tiles} query tiles (heads 0..{h - 1}) of the {w.name} workload, "
+                  f"float64 numpy, {t_used:.1f} s; a full call extrapolates to {full_s:.0f} s",
+        "seconds": t_used,
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this STA build runs on a single MI355X; "
+              "multi-GPU sharding is a design note only (heads shard with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sliding_tile_attention_sta_amd import api
+    from sliding_tile_attention_sta_amd.synthetic import WORKLOADS, make_qkv
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    q, k, v = make_qkv(w, dev)
+    plan = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    flops = plan.flops
+
+    def step():
+        api.sta_forward_plan(plan, q, k, v, out=out, scale=w.scale, layout="natural", stream=stream)
+
+    ms = timed(step, args.steps, args.warmup, stream)
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    # The step is a single launch of the forward kernel on `stream`, so the
+    # per-launch kernel duration is the event time per step.
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                t = json.load(f)
+            if t.get("workload") == w.name:
+                traffic = t.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "sta_fwd_kernel<128,3,8,bf16 in,f32 out>"}
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "video": list(w.video), "tile": list(w.tile),
+                   "windows": sorted({tuple(x) for x in w.windows}), "heads": w.heads,
+                   "head_dim": w.head_dim, "batch": w.batch, "layout": "natural",
+                   "out_dtype": "f32", "products": "QK^T bf16 MFMA, PV fp16 MFMA, fp32 accumulate",
+                   "flops_per_step": flops},
+        "roofline": roofline,
+    }
+
+    if not args.no_context:
+        # explicit reorder -> tile-major forward -> unreorder
+        qt, kt, vt = (api.sta_tile_reorder(plan, x) for x in (q, k, v))
+        out_t = torch.empty(qt.shape, dtype=torch.float32, device=dev)
+        out_n = torch.empty_like(out)
+
+        def reorder_in():
+            for x, y in ((q, qt), (k, kt), (v, vt)):
+                api.sta_tile_reorder(plan, x, out=y, stream=stream)
+
+        def fwd_tm():
+            api.sta_forward_plan(plan, qt, kt, vt, out=out_t, scale=w.scale, layout="tile_major",
+                                 stream=stream)
+
+        def unreorder_out():
+            api.sta_tile_unreorder(plan, out_t, out=out_n, stream=stream)
+
+        ms_r = timed(reorder_in, max(3, args.steps // 2), 1, stream)
+        ms_f = timed(fwd_tm, max(3, args.steps // 2), 1, stream)
+        ms_u = timed(unreorder_out, max(3, args.steps // 2), 1, stream)
+        bytes_r = 3 * 2 * q.numel() * q.element_size()
+        bytes_u = 2 * out_t.numel() * 4
+        result["reorder_path"] = {
+            "reorder_qkv_ms": round(ms_r, 4), "reorder_GBps": round(bytes_r / ms_r / 1e6, 1),
+            "forward_tile_major_ms": round(ms_f, 4),
+            "unreorder_o_ms": round(ms_u, 4), "unreorder_GBps": round(bytes_u / ms_u / 1e6, 1),
+            "total_ms": round(ms_r + ms_f + ms_u, 4),
+        }
+        del qt, kt, vt, out_t, out_n
+        # dense context: the same kernel with the window covering the whole grid
+        grid = tuple(e // t for e, t in zip(w.video, w.tile))
+        dplan = api.Plan(w.batch, w.heads, w.video, w.tile, [grid] * w.heads, w.head_dim)
+        ms_d = timed(lambda: api.sta_forward_plan(dplan, q, k, v, out=out, scale=w.scale,
+                                                  stream=stream), 3, 1, stream)
+        result["dense_context"] = {"ms": round(ms_d, 3),
+                                   "tflops": round(dplan.flops / (ms_d * 1e-3) / 1e12, 2),
+                                   "sta_speedup": round(ms_d / ms, 2)}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * sta.h -- C ABI of the MI355X (gfx950) Sliding Tile Attention forward library.
+ *
+ * Operation (source: "Fast Video Generation with Sliding Tile Attention",
+ * arXiv 2502.04507 -- index page, section "Abstract"; gptget summary page,
+ * sections "Methodology", "Technical Contribution" and "Novelty"):
+ * a T x H x W video latent is cut into non-overlapping tiles of
+ * tT x tH x tW tokens; every query tile attends to all tokens of exactly the
+ * key/value tiles inside its 3D window (a box of wT x wH x wW tiles, chosen
+ * per head), and to nothing else, so no (query tile, key tile) block is ever
+ * partly masked.  Inside the window it is ordinary softmax attention:
+ *
+ *     O[x] = sum_j softmax_j(scale * Q[x].K[j]) V[j],  j over the window.
+ *
+ * Window geometry: a window wider than the tile grid is clamped to it; the
+ * window of query tile c on an axis of n tiles starts at
+ * clamp(c - floor((w-1)/2), 0, n - w), so border windows shift inward and
+ * every query tile sees exactly wT*wH*wW key tiles.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are caller-owned DEVICE pointers, contiguous
+ *     [batch, heads, N, head_dim] with N = T*H*W tokens.  In
+ *     STA_LAYOUT_NATURAL the token axis is raster order (t, y, z), z fastest,
+ *     i.e. the tensor is [batch, heads, T, H, W, head_dim].  In
+ *     STA_LAYOUT_TILE_MAJOR each tile's tokens are contiguous: tiles in
+ *     raster order of tile coordinates, tokens inside a tile in raster order
+ *     of their local (t, y, z).
+ *   - out must not overlap any input.
+ *   - stream is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous with respect to the host; none synchronises.
+ *   - Every argument and shape check runs on the host before any launch, so a
+ *     call that returns an error has written nothing.
+ *   - Functions never throw; they return a sta_status.
+ *   - A plan is immutable after creation; it may be used from several host
+ *     threads and streams at once.  Its device tables are uploaded once per
+ *     device, on the first call that needs them.
+ */
+#ifndef STA_H
+#define STA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STA_OK = 0,
+  STA_ERR_ARG = -1,         /* null pointer, window < 1, bad enum, scale <= 0, ... */
+  STA_ERR_SHAPE = -2,       /* an extent is not a positive multiple of its tile size */
+  STA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128, or tile volume not a multiple of 32 */
+  STA_ERR_ALLOC = -4,       /* host or device allocation failed */
+  STA_ERR_HIP = -5          /* a HIP runtime call or a launch failed (incl. no device) */
+} sta_status;
+
+typedef enum { STA_BF16 = 0, STA_F32 = 1 } sta_dtype;
+
+typedef enum { STA_LAYOUT_NATURAL = 0, STA_LAYOUT_TILE_MAJOR = 1 } sta_layout;
+
+typedef struct sta_plan sta_plan; /* opaque, owned by the library */
+
+/* Read-only description of a plan (host memory, filled by sta_plan_get_info). */
+typedef struct {
+  int32_t batch, heads, T, H, W, head_dim;
+  int32_t tile[3];          /* tokens per tile on (T, H, W) */
+  int32_t grid[3];          /* tiles on (T, H, W) */
+  int32_t tile_tokens;      /* tT*tH*tW */
+  int32_t n_tiles;          /* grid[0]*grid[1]*grid[2] */
+  int64_t tokens;           /* T*H*W */
+  int64_t pairs;            /* attended (query tile, key tile) pairs, summed over heads, one batch element */
+  double flops;             /* 4 * tile_tokens^2 * head_dim * pairs * batch: FLOPs of the two products */
+  int64_t work_items;       /* launched work items (including idle padding items) */
+  int32_t queries_per_item; /* query tokens per work item */
+  int32_t kernel_variant;   /* 0 = generic (32 queries / item), 1 = 384-query items */
+} sta_plan_info;
+
+/* Build the host plan: tile grid, clamped per-head windows, per-(head, query
+ * tile) key-tile lists (raster order of tile coordinates) and the launch
+ * schedule (work items ordered by decreasing cost, spread evenly over the
+ * chip's XCDs).  Host work only; no device is touched.
+ *   window: heads*3 ints (wT, wH, wW) in tiles, >= 1; wider than the grid is clamped.
+ *   tile:   3 ints (tT, tH, tW) in tokens.
+ * Errors: STA_ERR_ARG (null, non-positive sizes or windows), STA_ERR_SHAPE
+ * (T, H or W not a multiple of its tile size), STA_ERR_UNSUPPORTED (head_dim
+ * not 64 or 128, tile volume not a multiple of 32), STA_ERR_ALLOC.
+ * On success *out owns the plan; release it with sta_plan_destroy. */
+sta_status sta_plan_create(int batch, int heads, int T, int H, int W, const int tile[3],
+                           const int *window, int head_dim, sta_plan **out);
+
+/* Release a plan and its device tables (NULL is a no-op).  The caller must
+ * make sure no launched work still uses the plan. */
+sta_status sta_plan_destroy(sta_plan *plan);
+
+/* Copy the plan description into *info (host). */
+sta_status sta_plan_get_info(const sta_plan *plan, sta_plan_info *info);
+
+/* Tile-major position -> natural token index, for all N tokens.
+ * perm: host buffer of at least cap int32.  STA_ERR_ARG if cap < N. */
+sta_status sta_plan_perm(const sta_plan *plan, int32_t *perm, int64_t cap);
+
+/* Key tiles (raster tile indices, ascending) of query tile q_tile for head
+ * head.  out: host buffer of cap int32; *count receives the list length even
+ * when it exceeds cap (then STA_ERR_ARG and out holds the first cap entries). */
+sta_status sta_plan_kv_tiles(const sta_plan *plan, int head, int q_tile, int32_t *out, int cap,
+                             int *count);
+
+/* The launch schedule: item codes in launch order, -1 for idle padding items.
+ * A code encodes ((b * heads + h) * n_tiles + q_tile) * subs + sub, where
+ * subs = tile_tokens / queries_per_item.  out: host buffer of cap int32;
+ * *count receives the item count (STA_ERR_ARG if it exceeds cap). */
+sta_status sta_plan_schedule(const sta_plan *plan, int32_t *out, int64_t cap, int64_t *count);
+
+/* Gather a [batch, heads, N, head_dim] tensor from natural into tile-major
+ * token order (out[.., p, :] = in[.., perm[p], :]), or back.  dtype is the
+ * element type of both tensors.  Bound by HBM bandwidth. */
+sta_status sta_tile_reorder(const sta_plan *plan, const void *in, void *out, sta_dtype dtype,
+                            void *stream);
+sta_status sta_tile_unreorder(const sta_plan *plan, const void *in, void *out, sta_dtype dtype,
+                              void *stream);
+
+/* STA forward with a plan.  q, k, v: [batch, heads, N, head_dim] of in_dtype
+ * (STA_F32 inputs are rounded to bf16, nearest-even, as they are loaded);
+ * out: same shape, out_dtype (STA_F32 or STA_BF16).  All four tensors use the
+ * token order given by layout.  scale > 0 multiplies Q.K (usually
+ * 1/sqrt(head_dim)).  Products run on bf16 MFMA with fp32 accumulation; the
+ * softmax runs in fp32. */
+sta_status sta_forward_plan(const sta_plan *plan, const void *q, const void *k, const void *v,
+                            void *out, float scale, sta_dtype in_dtype, sta_dtype out_dtype,
+                            sta_layout layout, void *stream);
+
+/* Same, building (or finding in a process-wide cache keyed by every shape
+ * and window argument) the plan itself.  Cached plans live until
+ * sta_clear_plan_cache or process exit. */
+sta_status sta_forward(const void *q, const void *k, const void *v, void *out, int batch, int heads,
+                       int T, int H, int W, const int tile[3], const int *window, int head_dim,
+                       float scale, sta_dtype in_dtype, sta_dtype out_dtype, sta_layout layout,
+                       void *stream);
+
+/* Destroy every cached plan.  Not safe while another thread is in sta_forward. */
+sta_status sta_clear_plan_cache(void);
+
+/* Static, human-readable name of a status code. */
+const char *sta_status_string(sta_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STA_H */

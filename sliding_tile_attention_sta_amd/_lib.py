@@ -1,0 +1,84 @@
+"""ctypes loader for libsta.so (argument marshalling only).
+
+Loading fails loudly when the library has not been built: there is no
+fallback of any kind.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsta.so")
+
+STA_OK, STA_ERR_ARG, STA_ERR_SHAPE, STA_ERR_UNSUPPORTED, STA_ERR_ALLOC, STA_ERR_HIP = 0, -1, -2, -3, -4, -5
+STA_BF16, STA_F32 = 0, 1
+STA_LAYOUT_NATURAL, STA_LAYOUT_TILE_MAJOR = 0, 1
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("H", ctypes.c_int32), ("W", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("tile", ctypes.c_int32 * 3), ("grid", ctypes.c_int32 * 3),
+        ("tile_tokens", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
+        ("tokens", ctypes.c_int64), ("pairs", ctypes.c_int64), ("flops", ctypes.c_double),
+        ("work_items", ctypes.c_int64), ("queries_per_item", ctypes.c_int32),
+        ("kernel_variant", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_IP = ctypes.POINTER(ctypes.c_int)
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+# name -> (restype, argtypes); every function declared in include/sta.h
+SIGNATURES = {
+    "sta_plan_create": (_I, [_I, _I, _I, _I, _I, _IP, _IP, _I, ctypes.POINTER(_P)]),
+    "sta_plan_destroy": (_I, [_P]),
+    "sta_plan_get_info": (_I, [_P, ctypes.POINTER(PlanInfo)]),
+    "sta_plan_perm": (_I, [_P, _I32P, _I64]),
+    "sta_plan_kv_tiles": (_I, [_P, _I, _I, _I32P, _I, _IP]),
+    "sta_plan_schedule": (_I, [_P, _I32P, _I64, ctypes.POINTER(_I64)]),
+    "sta_tile_reorder": (_I, [_P, _P, _P, _I, _P]),
+    "sta_tile_unreorder": (_I, [_P, _P, _P, _I, _P]),
+    "sta_forward_plan": (_I, [_P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I, _P]),
+    "sta_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _IP, _IP, _I, ctypes.c_float,
+                         _I, _I, _I, _P]),
+    "sta_clear_plan_cache": (_I, []),
+    "sta_status_string": (ctypes.c_char_p, [_I]),
+}
+
+_lib = None
+
+
+class StaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sliding_tile_attention_sta_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sta_status_string(status).decode()
+
+
+def check(status: int, where: str) -> None:
+    if status != STA_OK:
+        raise StaError(status, where)

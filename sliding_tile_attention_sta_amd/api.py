@@ -1,0 +1,196 @@
+"""Python binding of the STA C ABI (include/sta.h).
+
+Argument marshalling only: shapes, dtypes and device pointers of torch
+tensors are passed to libsta.so, which does every step of the computation
+in its own HIP kernels.  PyTorch provides device memory and the stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Sequence
+
+import torch
+
+from . import _lib as L
+
+__all__ = [
+    "Plan", "sta_plan_create", "sta_tile_reorder", "sta_tile_unreorder", "sta_forward_plan",
+    "sta_forward", "sta_clear_plan_cache", "StaError",
+]
+
+StaError = L.StaError
+
+_DTYPES = {torch.bfloat16: L.STA_BF16, torch.float32: L.STA_F32}
+_LAYOUTS = {"natural": L.STA_LAYOUT_NATURAL, "tile_major": L.STA_LAYOUT_TILE_MAJOR}
+
+
+def _ints(xs):
+    xs = [int(x) for x in xs]
+    return (ctypes.c_int * len(xs))(*xs)
+
+
+def _flat_windows(windows, heads: int):
+    ws = [tuple(int(v) for v in w) for w in windows]
+    if len(ws) == 1 and heads > 1:
+        ws = ws * heads
+    if len(ws) != heads or any(len(w) != 3 for w in ws):
+        raise ValueError("windows: one (wT, wH, wW) per head")
+    return [v for w in ws for v in w]
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """Owned sta_plan handle (host tables; device tables are uploaded lazily)."""
+
+    def __init__(self, batch: int, heads: int, video: Sequence[int], tile: Sequence[int],
+                 windows, head_dim: int):
+        h = ctypes.c_void_p()
+        T, H, W = (int(x) for x in video)
+        st = L.lib().sta_plan_create(int(batch), int(heads), T, H, W, _ints(tile),
+                                     _ints(_flat_windows(windows, heads)), int(head_dim),
+                                     ctypes.byref(h))
+        L.check(st, "sta_plan_create")
+        self._h = h
+        self._destroy = L.lib().sta_plan_destroy
+        self.info = L.PlanInfo()
+        L.check(L.lib().sta_plan_get_info(self._h, ctypes.byref(self.info)), "sta_plan_get_info")
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._destroy(h)
+            self._h = None
+
+    # -- host queries -------------------------------------------------------
+    @property
+    def tokens(self) -> int:
+        return int(self.info.tokens)
+
+    @property
+    def flops(self) -> float:
+        return float(self.info.flops)
+
+    def perm(self) -> torch.Tensor:
+        out = torch.empty(self.tokens, dtype=torch.int32)
+        L.check(L.lib().sta_plan_perm(self._h, ctypes.cast(out.data_ptr(), L._I32P), out.numel()),
+                "sta_plan_perm")
+        return out
+
+    def kv_tiles(self, head: int, q_tile: int) -> list[int]:
+        cnt = ctypes.c_int()
+        L.lib().sta_plan_kv_tiles(self._h, head, q_tile, None, 0, ctypes.byref(cnt))
+        buf = (ctypes.c_int32 * max(1, cnt.value))()
+        L.check(L.lib().sta_plan_kv_tiles(self._h, head, q_tile, buf, cnt.value, ctypes.byref(cnt)),
+                "sta_plan_kv_tiles")
+        return list(buf[:cnt.value])
+
+    def schedule(self) -> torch.Tensor:
+        n = ctypes.c_int64()
+        L.lib().sta_plan_schedule(self._h, None, 0, ctypes.byref(n))
+        out = torch.empty(n.value, dtype=torch.int32)
+        L.check(L.lib().sta_plan_schedule(self._h, ctypes.cast(out.data_ptr(), L._I32P), n.value,
+                                          ctypes.byref(n)), "sta_plan_schedule")
+        return out
+
+
+def sta_plan_create(batch, heads, video, tile, windows, head_dim) -> Plan:
+    return Plan(batch, heads, video, tile, windows, head_dim)
+
+
+def _check_tensor(x: torch.Tensor, plan: Plan, name: str):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"{name}: dtype must be bfloat16 or float32")
+    i = plan.info
+    if x.numel() != i.batch * i.heads * i.tokens * i.head_dim:
+        raise ValueError(f"{name}: expected {i.batch}x{i.heads}x{i.tokens}x{i.head_dim} elements")
+
+
+def _reorder(fn, plan: Plan, x: torch.Tensor, out, stream):
+    _check_tensor(x, plan, "x")
+    if out is None:
+        out = torch.empty_like(x)
+    _check_tensor(out, plan, "out")
+    if out.dtype != x.dtype:
+        raise ValueError("out must have the input's dtype")
+    L.check(fn(plan.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+               _DTYPES[x.dtype], _stream(stream)), fn.__name__)
+    return out
+
+
+def sta_tile_reorder(plan: Plan, x: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """Natural [B, heads, T, H, W, D] (or [B, heads, N, D]) -> tile-major [B, heads, N, D]."""
+    y = _reorder(L.lib().sta_tile_reorder, plan, x, out, stream)
+    return y.view(x.shape[0], x.shape[1], -1, x.shape[-1]) if out is None else y
+
+
+def sta_tile_unreorder(plan: Plan, x: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """Tile-major [B, heads, N, D] -> natural order, same element count."""
+    return _reorder(L.lib().sta_tile_unreorder, plan, x, out, stream)
+
+
+def sta_forward_plan(plan: Plan, q, k, v, out=None, scale: float | None = None,
+                     out_dtype=torch.float32, layout: str = "natural", stream=None):
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(x, plan, name)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _check_tensor(out, plan, "out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(plan.info.head_dim)
+    st = L.lib().sta_forward_plan(plan.handle, ctypes.c_void_p(q.data_ptr()),
+                                  ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                  ctypes.c_void_p(out.data_ptr()), float(scale), _DTYPES[q.dtype],
+                                  _DTYPES[out.dtype], _LAYOUTS[layout], _stream(stream))
+    L.check(st, "sta_forward_plan")
+    return out
+
+
+def sta_forward(q, k, v, tile, windows, scale: float | None = None, out=None,
+                out_dtype=torch.float32, layout: str = "natural", video=None, stream=None):
+    """STA forward through the library's plan cache.
+
+    q, k, v: [B, heads, T, H, W, D] (natural layout), or [B, heads, N, D]
+    with ``video=(T, H, W)``.  windows: one (wT, wH, wW) per head (or one for
+    all heads), in tiles."""
+    if q.dim() == 6:
+        B, heads, T, H, W, D = q.shape
+    else:
+        if video is None:
+            raise ValueError("video=(T, H, W) is required for 4-D inputs")
+        B, heads, _, D = q.shape
+        T, H, W = video
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if not x.is_cuda or not x.is_contiguous() or x.dtype not in _DTYPES or x.shape != q.shape:
+            raise ValueError(f"{name}: contiguous CUDA bf16/fp32 tensor shaped like q required")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = L.lib().sta_forward(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                             ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                             int(B), int(heads), int(T), int(H), int(W), _ints(tile),
+                             _ints(_flat_windows(windows, heads)), int(D), float(scale),
+                             _DTYPES[q.dtype], _DTYPES[out.dtype], _LAYOUTS[layout], _stream(stream))
+    L.check(st, "sta_forward")
+    return out
+
+
+def sta_clear_plan_cache() -> None:
+    L.check(L.lib().sta_clear_plan_cache(), "sta_clear_plan_cache")

@@ -1,0 +1,84 @@
+"""Build libsta.so (gfx950 HIP kernels + host plan) in-tree.
+
+Usage: python -m sliding_tile_attention_sta_amd.build [--jobs N]
+
+HIP sources are compiled by hipcc for gfx950 only; the host-only plan is
+compiled by g++.  Packed fp32 VALU forms are switched off for device code
+(``-target-feature -packed-fp32-ops``).  Objects go to ``_build/`` at the
+repository root; the shared library lands next to this file.
+"""
+
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libsta.so")
+
+HIP_SOURCES = ["sta_api.hip", "sta_forward.hip", "sta_reorder.hip"]
+CXX_SOURCES = ["sta_plan.cpp"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+    "-I", INCLUDE, "-I", CSRC,
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("build step failed:\n  " + " ".join(cmd) + "\n" + r.stdout)
+    return r.stdout
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD, exist_ok=True)
+    cmds, objs = [], []
+    for s in HIP_SOURCES:
+        o = os.path.join(BUILD, s + ".o")
+        cmds.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
+        objs.append(o)
+    for s in CXX_SOURCES:
+        o = os.path.join(BUILD, s + ".o")
+        cmds.append([CXX, *CXX_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
+        objs.append(o)
+    jobs = jobs or min(8, len(cmds))
+    with ThreadPoolExecutor(jobs) as ex:
+        outs = list(ex.map(_run, cmds))
+    if verbose:
+        for c, o in zip(cmds, outs):
+            print(" ".join(c))
+            if o.strip():
+                print(o)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("-v", "--verbose", action="store_true")
+    args = ap.parse_args(argv)
+    print(build(args.jobs, args.verbose))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

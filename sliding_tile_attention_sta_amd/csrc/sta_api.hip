@@ -1,0 +1,195 @@
+// C-ABI entry points that touch the GPU: device tables, reorder, forward,
+// and the process-wide plan cache.  Host-only plan code is in sta_plan.cpp.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "sta_internal.h"
+#include "sta_launch.h"
+
+namespace sta {
+namespace {
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Upload the plan's tables to the current device once; later calls reuse them.
+sta_status device_tables(const sta_plan *p, DeviceTables *out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return STA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(p->mu);
+  auto it = p->dev.find(dev);
+  if (it != p->dev.end()) {
+    *out = it->second;
+    return STA_OK;
+  }
+  std::vector<int32_t> base_tm(p->n_tiles), off_tm(p->V);
+  for (int i = 0; i < p->n_tiles; ++i) base_tm[i] = i * p->V;
+  for (int j = 0; j < p->V; ++j) off_tm[j] = j;
+  const std::vector<int32_t> *parts[] = {&p->kv_off, &p->kv_idx, &p->sched, &p->base_nat,
+                                         &p->off_nat, &base_tm, &off_tm};
+  size_t offs[7], total = 0;
+  for (int i = 0; i < 7; ++i) {
+    offs[i] = total;
+    total += (parts[i]->size() * sizeof(int32_t) + 255) & ~size_t(255);
+  }
+  void *block = nullptr;
+  if (hipMalloc(&block, total) != hipSuccess) return STA_ERR_ALLOC;
+  for (int i = 0; i < 7; ++i) {
+    if (parts[i]->empty()) continue;
+    if (hipMemcpy(static_cast<char *>(block) + offs[i], parts[i]->data(),
+                  parts[i]->size() * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(block);
+      return STA_ERR_HIP;
+    }
+  }
+  DeviceTables t;
+  char *b = static_cast<char *>(block);
+  t.kv_off = reinterpret_cast<int32_t *>(b + offs[0]);
+  t.kv_idx = reinterpret_cast<int32_t *>(b + offs[1]);
+  t.sched = reinterpret_cast<int32_t *>(b + offs[2]);
+  t.base_nat = reinterpret_cast<int32_t *>(b + offs[3]);
+  t.off_nat = reinterpret_cast<int32_t *>(b + offs[4]);
+  t.base_tm = reinterpret_cast<int32_t *>(b + offs[5]);
+  t.off_tm = reinterpret_cast<int32_t *>(b + offs[6]);
+  t.block = block;
+  p->dev[dev] = t;
+  *out = t;
+  return STA_OK;
+}
+
+bool valid_dtype(sta_dtype d) { return d == STA_BF16 || d == STA_F32; }
+size_t dtype_bytes(sta_dtype d) { return d == STA_F32 ? 4 : 2; }
+
+sta_status reorder(const sta_plan *p, const void *in, void *out, sta_dtype dtype, void *stream,
+                   int inverse) {
+  if (!p || !in || !out || !valid_dtype(dtype)) return STA_ERR_ARG;
+  const size_t bytes = (size_t)p->batch * p->heads * p->N * p->D * dtype_bytes(dtype);
+  if (overlaps(in, bytes, out, bytes)) return STA_ERR_ARG;
+  DeviceTables t;
+  sta_status st = device_tables(p, &t);
+  if (st != STA_OK) return st;
+  ReorderArgs a;
+  a.in = in;
+  a.out = out;
+  a.base = t.base_nat;
+  a.off = t.off_nat;
+  a.rows = (int64_t)p->batch * p->heads * p->N;
+  a.N = p->N;
+  a.V = p->V;
+  a.row_bytes = (int32_t)(p->D * dtype_bytes(dtype));
+  a.inverse = inverse;
+  return launch_reorder(a, static_cast<hipStream_t>(stream)) == hipSuccess ? STA_OK : STA_ERR_HIP;
+}
+
+struct CacheKey {
+  std::vector<int> v;
+  bool operator<(const CacheKey &o) const { return v < o.v; }
+};
+std::mutex g_cache_mu;
+std::map<CacheKey, sta_plan *> g_cache;
+
+}  // namespace
+
+void release_device_tables(sta_plan *p) {
+  std::lock_guard<std::mutex> lock(p->mu);
+  if (p->dev.empty()) return;
+  int cur = -1;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (auto &kv : p->dev) {
+    if (hipSetDevice(kv.first) == hipSuccess) (void)hipFree(kv.second.block);
+  }
+  if (have_cur) (void)hipSetDevice(cur);
+  p->dev.clear();
+}
+
+}  // namespace sta
+
+extern "C" {
+
+sta_status sta_tile_reorder(const sta_plan *plan, const void *in, void *out, sta_dtype dtype,
+                            void *stream) {
+  return sta::reorder(plan, in, out, dtype, stream, 0);
+}
+
+sta_status sta_tile_unreorder(const sta_plan *plan, const void *in, void *out, sta_dtype dtype,
+                              void *stream) {
+  return sta::reorder(plan, in, out, dtype, stream, 1);
+}
+
+sta_status sta_forward_plan(const sta_plan *p, const void *q, const void *k, const void *v,
+                            void *out, float scale, sta_dtype in_dtype, sta_dtype out_dtype,
+                            sta_layout layout, void *stream) {
+  if (!p || !q || !k || !v || !out) return STA_ERR_ARG;
+  if (!sta::valid_dtype(in_dtype) || !sta::valid_dtype(out_dtype)) return STA_ERR_ARG;
+  if (layout != STA_LAYOUT_NATURAL && layout != STA_LAYOUT_TILE_MAJOR) return STA_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return STA_ERR_ARG;
+  const size_t elems = (size_t)p->batch * p->heads * p->N * p->D;
+  const size_t ib = elems * sta::dtype_bytes(in_dtype), ob = elems * sta::dtype_bytes(out_dtype);
+  if (sta::overlaps(out, ob, q, ib) || sta::overlaps(out, ob, k, ib) || sta::overlaps(out, ob, v, ib))
+    return STA_ERR_ARG;
+  sta::DeviceTables t;
+  sta_status st = sta::device_tables(p, &t);
+  if (st != STA_OK) return st;
+  sta::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = out;
+  a.sched = t.sched;
+  a.kv_off = t.kv_off;
+  a.kv_idx = t.kv_idx;
+  a.base = layout == STA_LAYOUT_NATURAL ? t.base_nat : t.base_tm;
+  a.off = layout == STA_LAYOUT_NATURAL ? t.off_nat : t.off_tm;
+  a.heads = p->heads;
+  a.n_tiles = p->n_tiles;
+  a.V = p->V;
+  a.subs = p->subs;
+  a.N = p->N;
+  a.sl2e = scale * 1.44269504088896340736f;
+  a.n_blocks = (int32_t)p->sched.size();
+  hipError_t e = sta::launch_forward(a, p->variant, p->D, in_dtype == STA_F32, out_dtype == STA_F32,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? STA_OK : STA_ERR_HIP;
+}
+
+sta_status sta_forward(const void *q, const void *k, const void *v, void *out, int batch, int heads,
+                       int T, int H, int W, const int tile[3], const int *window, int head_dim,
+                       float scale, sta_dtype in_dtype, sta_dtype out_dtype, sta_layout layout,
+                       void *stream) {
+  if (!tile || !window || heads < 1) return STA_ERR_ARG;
+  sta::CacheKey key;
+  key.v = {batch, heads, T, H, W, tile[0], tile[1], tile[2], head_dim};
+  key.v.insert(key.v.end(), window, window + 3 * heads);
+  sta_plan *p = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(sta::g_cache_mu);
+    auto it = sta::g_cache.find(key);
+    if (it != sta::g_cache.end()) {
+      p = it->second;
+    } else {
+      sta_status st = sta::build_plan(batch, heads, T, H, W, tile, window, head_dim, &p);
+      if (st != STA_OK) return st;
+      try {
+        sta::g_cache[key] = p;
+      } catch (...) {
+        sta_plan_destroy(p);
+        return STA_ERR_ALLOC;
+      }
+    }
+  }
+  return sta_forward_plan(p, q, k, v, out, scale, in_dtype, out_dtype, layout, stream);
+}
+
+sta_status sta_clear_plan_cache(void) {
+  std::lock_guard<std::mutex> lock(sta::g_cache_mu);
+  for (auto &kv : sta::g_cache) sta_plan_destroy(kv.second);
+  sta::g_cache.clear();
+  return STA_OK;
+}
+
+}  // extern "C"

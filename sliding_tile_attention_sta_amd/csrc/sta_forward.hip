@@ -1,0 +1,320 @@
+// Sliding Tile Attention forward for gfx950 (MI355X).
+//
+// What is computed ("Fast Video Generation with Sliding Tile Attention",
+// arXiv 2502.04507, index page, Abstract; gptget summary page, Methodology and
+// Novelty): every query tile attends to the whole key/value tiles of its 3D
+// window and to nothing else.  Because a (query tile, key tile) pair is
+// either fully attended or skipped, the kernel never evaluates a mask: it
+// walks the key-tile list of its query tile and runs dense blocks.  The
+// summary page credits the original kernel's speed to dense computation on
+// the sparse pattern in the FlashAttention line (online softmax over
+// streamed key blocks); this kernel keeps that idea and is otherwise laid
+// out for CDNA4:
+//
+//   * One work group owns QPI query tokens of one (batch, head, query tile)
+//     and keeps them for the whole window; each wave owns 16*QB queries.
+//   * Scores are computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_16x16x32_bf16: K comes from LDS, Q stays in VGPRs.  In the
+//     accumulator layout a lane holds one query and 4 keys of each 16x16
+//     block, so the row max and row sum are in-lane reductions plus two
+//     lane swaps (v_permlane16_swap, v_permlane32_swap).
+//   * The softmax is online, in fp32, with exp2 and the scale folded into
+//     one FMA; probabilities (in [0, 1]) are rounded to fp16, nearest even,
+//     straight into the B operand of the second product.  fp16 keeps 11
+//     significant bits against bf16's 8, which cuts the error of the
+//     weighted sum about tenfold when a few keys dominate a row.
+//   * O^T += V^T P^T on v_mfma_f32_16x16x32_f16.  V is converted to fp16 as
+//     it is staged into LDS (exact for bf16 values up to 65504 in
+//     magnitude; larger ones saturate).  The V^T operand is read from
+//     row-major V in LDS with ds_read_b64_tr_b16, which transposes 4x16
+//     16-bit blocks inside each 16-lane group, so V is never transposed in
+//     memory.
+//   * K and V advance 32 keys at a time through a two-stage LDS ring; the
+//     next block's global loads are issued before the current block's math.
+//   * Rows are located through two small tables (tile base row, tile-local
+//     row offset), so one kernel reads and writes either the natural
+//     [T, H, W] token order or the tile-major order.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sta_launch.h"
+
+namespace sta {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int KB = 32;  // keys per pipeline step
+
+__device__ __forceinline__ float swap_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float swap_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 8 consecutive elements at p as bf16 (fp32 inputs are rounded to nearest even).
+template <bool F32>
+__device__ __forceinline__ uint4 load8(const void *p) {
+  if constexpr (F32) {
+    const float4 *f = reinterpret_cast<const float4 *>(p);
+    float4 x = f[0], y = f[1];
+    bf16x8 r;
+    r[0] = (__bf16)x.x; r[1] = (__bf16)x.y; r[2] = (__bf16)x.z; r[3] = (__bf16)x.w;
+    r[4] = (__bf16)y.x; r[5] = (__bf16)y.y; r[6] = (__bf16)y.z; r[7] = (__bf16)y.w;
+    return __builtin_bit_cast(uint4, r);
+  } else {
+    return *reinterpret_cast<const uint4 *>(p);
+  }
+}
+
+// 8 consecutive elements at p as fp16 for the P.V product.  bf16 values
+// inside the fp16 range convert exactly; magnitudes beyond 65504 saturate
+// (no infinities); fp32 inputs are rounded to nearest even.
+__device__ __forceinline__ float sat16(float x) { return __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f); }
+
+template <bool F32>
+__device__ __forceinline__ uint4 load8_f16(const void *p) {
+  f16x8 r;
+  if constexpr (F32) {
+    const float4 *f = reinterpret_cast<const float4 *>(p);
+    float4 x = f[0], y = f[1];
+    r[0] = (_Float16)sat16(x.x); r[1] = (_Float16)sat16(x.y); r[2] = (_Float16)sat16(x.z); r[3] = (_Float16)sat16(x.w);
+    r[4] = (_Float16)sat16(y.x); r[5] = (_Float16)sat16(y.y); r[6] = (_Float16)sat16(y.z); r[7] = (_Float16)sat16(y.w);
+  } else {
+    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (_Float16)sat16((float)b[i]);
+  }
+  return __builtin_bit_cast(uint4, r);
+}
+
+// D: head dim.  QB: 16-query blocks per wave.  NW: waves per group.
+template <int D, int QB, int NW, bool F32IN, bool F32OUT>
+__global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int QPI = 16 * QB * NW;               // queries per work item
+  constexpr int KSTR = D * 2 + 16;                // LDS row stride (bytes), padded
+  constexpr int VSTR = D * 2 + 16;
+  constexpr int KST_BYTES = KB * KSTR;
+  constexpr int VST_BYTES = KB * VSTR;
+  constexpr int CHUNKS = KB * D / 8;              // 8-element chunks per tensor per step
+  constexpr int CPT = (CHUNKS + NT - 1) / NT;     // chunks per thread per tensor
+  static_assert(CHUNKS % NT == 0 || CHUNKS < NT, "chunk split");
+  constexpr int EB = F32IN ? 4 : 2;               // input element bytes
+  constexpr int DC = D / 32;                      // 32-wide d chunks (QK^T K-dim steps)
+  constexpr int DB = D / 16;                      // 16-wide d blocks (rows of O^T)
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * KST_BYTES + 2 * VST_BYTES];
+
+  const int item = a.sched[blockIdx.x];
+  if (item < 0) return;
+  const int sub = item % a.subs;
+  const int rest = item / a.subs;
+  const int qt = rest % a.n_tiles;
+  const int bh = rest / a.n_tiles;
+  const int h = bh % a.heads;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+
+  const char *qg = reinterpret_cast<const char *>(a.q) + (size_t)bh * a.N * D * EB;
+  const char *kg = reinterpret_cast<const char *>(a.k) + (size_t)bh * a.N * D * EB;
+  const char *vg = reinterpret_cast<const char *>(a.v) + (size_t)bh * a.N * D * EB;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), kept in VGPRs --------------
+  bf16x8 qf[QB][DC];
+  const int qbase = a.base[qt];
+  const int qloc0 = sub * QPI + wave * 16 * QB;
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const int row = qbase + a.off[qloc0 + 16 * j + l16];
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+      qf[j][c] = __builtin_bit_cast(bf16x8, load8<F32IN>(qg + ((size_t)row * D + 32 * c + 8 * g) * EB));
+  }
+
+  // ---- key-tile walk ------------------------------------------------------
+  const int kv0 = a.kv_off[h * a.n_tiles + qt];
+  const int nkv = a.kv_off[h * a.n_tiles + qt + 1] - kv0;
+  const int steps_per_tile = a.V / KB;
+  const int nsteps = nkv * steps_per_tile;
+
+  uint4 pk[CPT], pv[CPT];
+  auto fetch = [&](int s) {
+    const int tile = a.kv_idx[kv0 + s / steps_per_tile];
+    const int loc0 = (s % steps_per_tile) * KB;
+    const int tb = a.base[tile];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS < NT && c >= CHUNKS) break;
+      const int r = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      const size_t e = (size_t)(tb + a.off[loc0 + r]) * D + col;
+      pk[i] = load8<F32IN>(kg + e * EB);
+      pv[i] = load8_f16<F32IN>(vg + e * EB);
+    }
+  };
+  auto stash = [&](int stage) {
+    char *ks = smem + stage * KST_BYTES;
+    char *vs = smem + 2 * KST_BYTES + stage * VST_BYTES;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS < NT && c >= CHUNKS) break;
+      const int r = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      *reinterpret_cast<uint4 *>(ks + r * KSTR + col * 2) = pk[i];
+      *reinterpret_cast<uint4 *>(vs + r * VSTR + col * 2) = pv[i];
+    }
+  };
+
+  f32x4 o[DB][QB];
+  float m[QB], l[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl2e = a.sl2e;
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+
+  for (int s = 0; s < nsteps; ++s) {
+    const int stage = s & 1;
+    if (s + 1 < nsteps) fetch(s + 1);
+    const char *ks = smem + stage * KST_BYTES;
+    const char *vs = smem + 2 * KST_BYTES + stage * VST_BYTES;
+
+    // S^T[key][query] for 32 keys (two 16-key blocks) x 16*QB queries.
+    f32x4 st[2][QB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int j = 0; j < QB; ++j) st[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(ks + (kb * 16 + l16) * KSTR + (32 * c + 8 * g) * 2);
+#pragma unroll
+        for (int j = 0; j < QB; ++j)
+          st[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[j][c], st[kb][j], 0, 0, 0);
+      }
+    }
+
+    // Online softmax; lane holds query 16j + l16, keys 4g + r and 16 + 4g + r.
+    f16x8 pb[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      float mx = fmaxf(fmaxf(fmaxf(st[0][j][0], st[0][j][1]), fmaxf(st[0][j][2], st[0][j][3])),
+                       fmaxf(fmaxf(st[1][j][0], st[1][j][1]), fmaxf(st[1][j][2], st[1][j][3])));
+      mx = swap_max(mx);
+      const float mnew = fmaxf(m[j], mx);
+      const float alpha = __builtin_amdgcn_exp2f((m[j] - mnew) * sl2e);
+      m[j] = mnew;
+      const float mb = mnew * sl2e;
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r], sl2e, -mb));
+          ps += p;
+          pb[j][kb * 4 + r] = (_Float16)p;
+        }
+      l[j] = l[j] * alpha + ps;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) o[b][j] *= alpha;
+    }
+
+    // O^T[d][query] += V^T P^T.
+    const int trow = 4 * g + (l16 >> 2);
+    const int tcol = 4 * (l16 & 3);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const lds_char *vb = (const lds_char *)(vs) + b * 32 + tcol * 2;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vb + trow * VSTR));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vb + (trow + 16) * VSTR));
+      f16x8 va;
+      const f16x4 lob = __builtin_bit_cast(f16x4, lo), hib = __builtin_bit_cast(f16x4, hi);
+      va[0] = lob[0]; va[1] = lob[1]; va[2] = lob[2]; va[3] = lob[3];
+      va[4] = hib[0]; va[5] = hib[1]; va[6] = hib[2]; va[7] = hib[3];
+#pragma unroll
+      for (int j = 0; j < QB; ++j) o[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[j], o[b][j], 0, 0, 0);
+    }
+
+    if (s + 1 < nsteps) stash(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- finalize: O = O^T / l, stored row-major ----------------------------
+  char *og = reinterpret_cast<char *>(a.o) + (size_t)bh * a.N * D * (F32OUT ? 4 : 2);
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const float inv = 1.f / swap_sum(l[j]);
+    const int row = qbase + a.off[qloc0 + 16 * j + l16];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const f32x4 r = o[b][j] * inv;
+      const size_t e = (size_t)row * D + b * 16 + 4 * g;
+      if constexpr (F32OUT) {
+        *reinterpret_cast<f32x4 *>(og + e * 4) = r;
+      } else {
+        bf16x4 rb;
+        rb[0] = (__bf16)r[0]; rb[1] = (__bf16)r[1]; rb[2] = (__bf16)r[2]; rb[3] = (__bf16)r[3];
+        *reinterpret_cast<bf16x4 *>(og + e * 2) = rb;
+      }
+    }
+  }
+}
+
+template <int D, int QB, int NW>
+hipError_t launch_io(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s) {
+  dim3 grid(a.n_blocks), block(NW * 64);
+  if (f32_in) {
+    if (f32_out) hipLaunchKernelGGL((sta_fwd_kernel<D, QB, NW, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((sta_fwd_kernel<D, QB, NW, true, false>), grid, block, 0, s, a);
+  } else {
+    if (f32_out) hipLaunchKernelGGL((sta_fwd_kernel<D, QB, NW, false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((sta_fwd_kernel<D, QB, NW, false, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_forward(const FwdArgs &a, int variant, int head_dim, bool f32_in, bool f32_out,
+                          hipStream_t stream) {
+  if (a.n_blocks <= 0) return hipSuccess;
+  if (variant == 1) {
+    if (head_dim == 128) return launch_io<128, 3, 8>(a, f32_in, f32_out, stream);
+    return launch_io<64, 3, 8>(a, f32_in, f32_out, stream);
+  }
+  if (head_dim == 128) return launch_io<128, 1, 2>(a, f32_in, f32_out, stream);
+  return launch_io<64, 1, 2>(a, f32_in, f32_out, stream);
+}
+
+}  // namespace sta

@@ -1,0 +1,67 @@
+// Internal definitions shared by the host plan (sta_plan.cpp) and the HIP
+// entry points (sta_api.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "sta.h"
+
+namespace sta {
+
+// Kernel variants: how many query tokens one work group owns.
+enum Variant : int32_t {
+  kGeneric = 0,   // 32 queries per work item (2 waves x 16); any tile volume % 32 == 0
+  kTile384 = 1,   // 384 queries per work item (8 waves x 48); tile volume % 384 == 0
+};
+
+constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, blocks dispatched round-robin
+constexpr int kKeyBlock = 32;     // keys staged in LDS per pipeline step
+constexpr int kMaxTileTokens = 4096;
+
+struct DeviceTables {
+  int32_t *kv_off = nullptr;       // heads*n_tiles + 1
+  int32_t *kv_idx = nullptr;       // sum of list lengths
+  int32_t *sched = nullptr;        // work items in launch order (-1 = idle)
+  int32_t *base_nat = nullptr;     // n_tiles: first token row of each tile, natural order
+  int32_t *off_nat = nullptr;      // tile_tokens: row offset of each tile-local token, natural order
+  int32_t *base_tm = nullptr;      // n_tiles: tile * tile_tokens
+  int32_t *off_tm = nullptr;       // tile_tokens: identity
+  void *block = nullptr;           // the single allocation holding all of the above
+};
+
+}  // namespace sta
+
+struct sta_plan {
+  int32_t batch = 0, heads = 0, T = 0, H = 0, W = 0, D = 0;
+  int32_t tile[3] = {0, 0, 0};
+  int32_t grid[3] = {0, 0, 0};
+  int32_t V = 0;          // tokens per tile
+  int32_t n_tiles = 0;
+  int64_t N = 0;          // tokens
+  std::vector<int32_t> win;       // heads*3 effective (clamped) windows
+  std::vector<int32_t> kv_off;    // heads*n_tiles + 1
+  std::vector<int32_t> kv_idx;    // key tiles per (head, query tile), launch order
+  std::vector<int32_t> sched;     // launch order of work items, -1 = idle
+  std::vector<int32_t> base_nat, off_nat;
+  int64_t pairs = 0;
+  int32_t variant = 0;
+  int32_t qpi = 0;        // queries per work item
+  int32_t subs = 0;       // work items per (b, head, query tile)
+
+  mutable std::mutex mu;
+  mutable std::map<int, sta::DeviceTables> dev;   // per HIP device ordinal
+};
+
+namespace sta {
+
+// Host-only plan construction (no HIP calls).  Defined in sta_plan.cpp.
+sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[3],
+                      const int *window, int head_dim, sta_plan **out);
+
+// Releases device tables; defined in sta_api.hip (needs HIP).
+void release_device_tables(sta_plan *plan);
+
+}  // namespace sta

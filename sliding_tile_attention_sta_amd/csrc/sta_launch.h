@@ -1,0 +1,42 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace sta {
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *o;
+  const int32_t *sched;    // work items in launch order (-1 = idle)
+  const int32_t *kv_off;   // heads*n_tiles + 1
+  const int32_t *kv_idx;   // key tiles of each (head, query tile)
+  const int32_t *base;     // n_tiles: first token row of each tile in the tensors' layout
+  const int32_t *off;      // tile_tokens: row offset of each tile-local token
+  int32_t heads, n_tiles, V, subs;
+  int64_t N;               // tokens per (batch, head)
+  float sl2e;              // softmax scale * log2(e)
+  int32_t n_blocks;        // length of sched
+};
+
+// Launch the forward kernel.  variant: 0 generic, 1 384-query items.
+hipError_t launch_forward(const FwdArgs &a, int variant, int head_dim, bool f32_in, bool f32_out,
+                          hipStream_t stream);
+
+struct ReorderArgs {
+  const void *in;
+  void *out;
+  const int32_t *base;     // natural-order base row of each tile
+  const int32_t *off;      // natural-order offset of each tile-local token
+  int64_t rows;            // batch*heads*N
+  int64_t N;
+  int32_t V;
+  int32_t row_bytes;       // head_dim * element size, a multiple of 16
+  int32_t inverse;         // 0: natural -> tile-major, 1: tile-major -> natural
+};
+
+hipError_t launch_reorder(const ReorderArgs &a, hipStream_t stream);
+
+}  // namespace sta

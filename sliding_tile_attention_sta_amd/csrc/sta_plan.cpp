@@ -1,0 +1,225 @@
+// Host-side planning for Sliding Tile Attention (no HIP calls in this file).
+//
+// Geometry follows the STA definition ("Fast Video Generation with Sliding
+// Tile Attention", arXiv 2502.04507: index page, Abstract; gptget summary
+// page, Methodology and Novelty): non-overlapping 3D tiles, a per-head window
+// of whole tiles that slides tile by tile.  Readings where the pages are
+// silent: windows wider than the grid are clamped to it, and a window is
+// centred on its query tile and shifted inward at the borders.
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <numeric>
+
+#include "sta_internal.h"
+
+namespace sta {
+namespace {
+
+inline int window_start(int c, int w, int n) {
+  int s = c - (w - 1) / 2;
+  if (s < 0) s = 0;
+  if (s > n - w) s = n - w;
+  return s;
+}
+
+// Work items in launch order.  Items are sorted by decreasing cost (number
+// of key tiles), cut into chunks of consecutive items, and each chunk goes to
+// the XCD with the least accumulated cost.  Blocks are dispatched to XCDs
+// round-robin (block b runs on XCD b % 8), so XCD x's queue is placed at
+// blocks x, x + 8, x + 16, ...  Within an XCD the hardware hands blocks to
+// free compute units in order, which is list scheduling of a
+// decreasing-cost list.  Chunks keep spatially adjacent query tiles of one
+// head on the same XCD, whose L2 then serves their overlapping windows.
+void build_schedule(sta_plan *p) {
+  const int64_t n_items = (int64_t)p->batch * p->heads * p->n_tiles * p->subs;
+  std::vector<int64_t> order(n_items);
+  std::iota(order.begin(), order.end(), 0);
+  auto cost = [&](int64_t code) {
+    int64_t rest = code / p->subs;
+    int qt = (int)(rest % p->n_tiles);
+    int h = (int)((rest / p->n_tiles) % p->heads);
+    return p->kv_off[h * p->n_tiles + qt + 1] - p->kv_off[h * p->n_tiles + qt];
+  };
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int64_t a, int64_t b) { return cost(a) > cost(b); });
+
+  const int64_t chunk = 32;  // compute units per XCD
+  std::vector<std::vector<int32_t>> queue(kXcds);
+  std::vector<int64_t> load(kXcds, 0);
+  for (int64_t i = 0; i < n_items; i += chunk) {
+    int64_t end = std::min(n_items, i + chunk);
+    int64_t c = 0;
+    for (int64_t j = i; j < end; ++j) c += cost(order[j]);
+    int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[x] += c;
+    for (int64_t j = i; j < end; ++j) queue[x].push_back((int32_t)order[j]);
+  }
+  size_t len = 0;
+  for (auto &q : queue) len = std::max(len, q.size());
+  p->sched.assign(len * kXcds, -1);
+  for (int x = 0; x < kXcds; ++x)
+    for (size_t s = 0; s < queue[x].size(); ++s) p->sched[s * kXcds + x] = queue[x][s];
+}
+
+}  // namespace
+
+sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[3],
+                      const int *window, int head_dim, sta_plan **out) {
+  if (!out || !tile || !window) return STA_ERR_ARG;
+  *out = nullptr;
+  if (batch < 1 || heads < 1 || T < 1 || H < 1 || W < 1) return STA_ERR_ARG;
+  for (int d = 0; d < 3; ++d)
+    if (tile[d] < 1) return STA_ERR_ARG;
+  for (int i = 0; i < heads * 3; ++i)
+    if (window[i] < 1) return STA_ERR_ARG;
+  const int ext[3] = {T, H, W};
+  for (int d = 0; d < 3; ++d)
+    if (ext[d] % tile[d] != 0) return STA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return STA_ERR_UNSUPPORTED;
+  const int64_t V64 = (int64_t)tile[0] * tile[1] * tile[2];
+  if (V64 % kKeyBlock != 0 || V64 > kMaxTileTokens) return STA_ERR_UNSUPPORTED;
+  const int64_t N64 = (int64_t)T * H * W;
+  // Element offsets are 64-bit in the kernels; token rows and table entries are int32.
+  if (N64 * batch * heads > (int64_t)INT32_MAX) return STA_ERR_UNSUPPORTED;
+
+  sta_plan *p = new (std::nothrow) sta_plan();
+  if (!p) return STA_ERR_ALLOC;
+  try {
+    p->batch = batch; p->heads = heads; p->T = T; p->H = H; p->W = W; p->D = head_dim;
+    for (int d = 0; d < 3; ++d) { p->tile[d] = tile[d]; p->grid[d] = ext[d] / tile[d]; }
+    p->V = (int32_t)V64;
+    p->N = N64;
+    p->n_tiles = p->grid[0] * p->grid[1] * p->grid[2];
+    if (p->V % 384 == 0) {
+      p->variant = kTile384; p->qpi = 384;
+    } else {
+      p->variant = kGeneric; p->qpi = 32;
+    }
+    p->subs = p->V / p->qpi;
+
+    // Per-head clamped windows and per-(head, query tile) key-tile lists.
+    // Launch order inside a window: raster order of (a mod wT, b mod wH,
+    // c mod wW).  The map from a tile coordinate to its residue is one-to-one
+    // on any w consecutive tiles, so query tiles whose windows overlap visit
+    // their shared key tiles at the same step, which the L2 rewards.
+    p->win.resize(heads * 3);
+    p->kv_off.assign((size_t)heads * p->n_tiles + 1, 0);
+    const int nT = p->grid[0], nH = p->grid[1], nW = p->grid[2];
+    for (int h = 0; h < heads; ++h) {
+      int w[3];
+      for (int d = 0; d < 3; ++d) w[d] = std::min(window[h * 3 + d], p->grid[d]);
+      for (int d = 0; d < 3; ++d) p->win[h * 3 + d] = w[d];
+      for (int qt = 0; qt < p->n_tiles; ++qt) {
+        const int ct = qt / (nH * nW), cy = (qt / nW) % nH, cz = qt % nW;
+        const int st = window_start(ct, w[0], nT), sy = window_start(cy, w[1], nH),
+                  sz = window_start(cz, w[2], nW);
+        for (int rt = 0; rt < w[0]; ++rt)
+          for (int ry = 0; ry < w[1]; ++ry)
+            for (int rz = 0; rz < w[2]; ++rz) {
+              // the tile in [s, s + w) whose coordinate is congruent to r mod w
+              const int a = st + ((rt - st % w[0]) % w[0] + w[0]) % w[0];
+              const int b = sy + ((ry - sy % w[1]) % w[1] + w[1]) % w[1];
+              const int c = sz + ((rz - sz % w[2]) % w[2] + w[2]) % w[2];
+              p->kv_idx.push_back((a * nH + b) * nW + c);
+            }
+        p->kv_off[(size_t)h * p->n_tiles + qt + 1] = (int32_t)p->kv_idx.size();
+      }
+    }
+    p->pairs = (int64_t)p->kv_idx.size();
+
+    // Token row tables for the natural layout.
+    p->base_nat.resize(p->n_tiles);
+    for (int qt = 0; qt < p->n_tiles; ++qt) {
+      const int ct = qt / (nH * nW), cy = (qt / nW) % nH, cz = qt % nW;
+      p->base_nat[qt] = ((ct * tile[0]) * H + cy * tile[1]) * W + cz * tile[2];
+    }
+    p->off_nat.resize(p->V);
+    for (int j = 0; j < p->V; ++j) {
+      const int lt = j / (tile[1] * tile[2]), ly = (j / tile[2]) % tile[1], lz = j % tile[2];
+      p->off_nat[j] = (lt * H + ly) * W + lz;
+    }
+    build_schedule(p);
+  } catch (const std::bad_alloc &) {
+    delete p;
+    return STA_ERR_ALLOC;
+  }
+  *out = p;
+  return STA_OK;
+}
+
+}  // namespace sta
+
+extern "C" {
+
+sta_status sta_plan_create(int batch, int heads, int T, int H, int W, const int tile[3],
+                           const int *window, int head_dim, sta_plan **out) {
+  return sta::build_plan(batch, heads, T, H, W, tile, window, head_dim, out);
+}
+
+sta_status sta_plan_destroy(sta_plan *plan) {
+  if (!plan) return STA_OK;
+  sta::release_device_tables(plan);
+  delete plan;
+  return STA_OK;
+}
+
+sta_status sta_plan_get_info(const sta_plan *p, sta_plan_info *info) {
+  if (!p || !info) return STA_ERR_ARG;
+  std::memset(info, 0, sizeof(*info));
+  info->batch = p->batch; info->heads = p->heads;
+  info->T = p->T; info->H = p->H; info->W = p->W; info->head_dim = p->D;
+  for (int d = 0; d < 3; ++d) { info->tile[d] = p->tile[d]; info->grid[d] = p->grid[d]; }
+  info->tile_tokens = p->V;
+  info->n_tiles = p->n_tiles;
+  info->tokens = p->N;
+  info->pairs = p->pairs;
+  info->flops = 4.0 * (double)p->V * (double)p->V * (double)p->D * (double)p->pairs * p->batch;
+  info->work_items = (int64_t)p->sched.size();
+  info->queries_per_item = p->qpi;
+  info->kernel_variant = p->variant;
+  return STA_OK;
+}
+
+sta_status sta_plan_perm(const sta_plan *p, int32_t *perm, int64_t cap) {
+  if (!p || !perm || cap < p->N) return STA_ERR_ARG;
+  for (int qt = 0; qt < p->n_tiles; ++qt)
+    for (int j = 0; j < p->V; ++j) perm[(int64_t)qt * p->V + j] = p->base_nat[qt] + p->off_nat[j];
+  return STA_OK;
+}
+
+sta_status sta_plan_kv_tiles(const sta_plan *p, int head, int q_tile, int32_t *out, int cap,
+                             int *count) {
+  if (!p || !count || head < 0 || head >= p->heads || q_tile < 0 || q_tile >= p->n_tiles)
+    return STA_ERR_ARG;
+  const size_t i = (size_t)head * p->n_tiles + q_tile;
+  std::vector<int32_t> list(p->kv_idx.begin() + p->kv_off[i], p->kv_idx.begin() + p->kv_off[i + 1]);
+  std::sort(list.begin(), list.end());
+  *count = (int)list.size();
+  if (!out && cap > 0) return STA_ERR_ARG;
+  for (int j = 0; j < cap && j < (int)list.size(); ++j) out[j] = list[j];
+  return (int)list.size() > cap ? STA_ERR_ARG : STA_OK;
+}
+
+sta_status sta_plan_schedule(const sta_plan *p, int32_t *out, int64_t cap, int64_t *count) {
+  if (!p || !count) return STA_ERR_ARG;
+  *count = (int64_t)p->sched.size();
+  if (cap < *count || !out) return STA_ERR_ARG;
+  std::memcpy(out, p->sched.data(), p->sched.size() * sizeof(int32_t));
+  return STA_OK;
+}
+
+const char *sta_status_string(sta_status s) {
+  switch (s) {
+    case STA_OK: return "STA_OK";
+    case STA_ERR_ARG: return "STA_ERR_ARG: invalid argument";
+    case STA_ERR_SHAPE: return "STA_ERR_SHAPE: extent not a multiple of the tile size";
+    case STA_ERR_UNSUPPORTED: return "STA_ERR_UNSUPPORTED: unsupported head_dim or tile volume";
+    case STA_ERR_ALLOC: return "STA_ERR_ALLOC: allocation failed";
+    case STA_ERR_HIP: return "STA_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "unknown sta_status";
+}
+
+}  // extern "C"

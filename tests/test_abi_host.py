@@ -1,0 +1,190 @@
+"""Host-side checks of libsta.so (CPU only; no kernel is launched).
+
+* the library loads and exports every function that include/sta.h declares;
+* the plan's key-tile lists, permutation and schedule agree with the
+  oracle's geometry (window starts, tile coordinates);
+* every invalid argument returns its status code before any device work.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import sta_oracle as O
+from sliding_tile_attention_sta_amd import _lib as L
+from sliding_tile_attention_sta_amd import api
+from sliding_tile_attention_sta_amd.synthetic import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "sta.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sta_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = header_functions()
+    for required in ["sta_plan_create", "sta_plan_destroy", "sta_forward", "sta_forward_plan",
+                     "sta_tile_reorder", "sta_tile_unreorder", "sta_status_string"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), f"{name} declared in sta.h but not exported"
+    assert set(header_functions()) == set(L.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings():
+    for code in [L.STA_OK, L.STA_ERR_ARG, L.STA_ERR_SHAPE, L.STA_ERR_UNSUPPORTED, L.STA_ERR_ALLOC,
+                 L.STA_ERR_HIP]:
+        s = L.status_string(code)
+        assert s.startswith("STA_")
+    assert "unknown" in L.status_string(42)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "720p", "mixed", "long"])
+def test_plan_matches_oracle_geometry(name):
+    w = WORKLOADS[name]
+    p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    grid = O.tile_grid(w.video, w.tile)
+    info = p.info
+    assert tuple(info.grid) == grid
+    assert info.tile_tokens == w.tile[0] * w.tile[1] * w.tile[2]
+    assert info.flops == O.sta_flops(w.video, w.tile, w.windows, w.head_dim, w.batch)
+    nT, nH, nW = grid
+    heads = range(w.heads) if w.heads <= 8 else range(0, w.heads, 5)
+    for h in heads:
+        for qt in range(0, nT * nH * nW, 7 if nT * nH * nW > 64 else 1):
+            c = (qt // (nH * nW), (qt // nW) % nH, qt % nW)
+            (t0, t1), (y0, y1), (z0, z1) = O.window_tiles(c, w.windows[h], grid)
+            want = sorted((a * nH + b) * nW + cc for a in range(t0, t1) for b in range(y0, y1)
+                          for cc in range(z0, z1))
+            assert p.kv_tiles(h, qt) == want
+
+
+def test_perm_is_the_tile_major_order():
+    w = WORKLOADS["tiny"]
+    p = api.Plan(1, 2, w.video, w.tile, w.windows, w.head_dim)
+    perm = p.perm().numpy()
+    coords = O.natural_coords(w.video)
+    T, H, W = w.video
+    tT, tH, tW = w.tile
+    grid = O.tile_grid(w.video, w.tile)
+    assert sorted(perm.tolist()) == list(range(T * H * W))
+    V = tT * tH * tW
+    for pos, n in enumerate(perm):
+        t, y, z = coords[n]
+        tile = ((t // tT) * grid[1] + y // tH) * grid[2] + z // tW
+        local = ((t % tT) * tH + y % tH) * tW + z % tW
+        assert pos == tile * V + local
+
+
+@pytest.mark.parametrize("name", ["720p", "mixed", "long", "small", "tiny"])
+def test_schedule_covers_every_item_once_and_balances_xcds(name):
+    w = WORKLOADS[name]
+    p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    s = p.schedule().numpy()
+    info = p.info
+    subs = info.tile_tokens // info.queries_per_item
+    n_items = w.batch * w.heads * info.n_tiles * subs
+    real = s[s >= 0]
+    assert sorted(real.tolist()) == list(range(n_items))
+    assert (s[s < 0] == -1).all()
+    assert len(s) % 8 == 0
+    # per-XCD cost (block b runs on XCD b % 8): spread within one chunk of items
+    cost = {}
+    grid = O.tile_grid(w.video, w.tile)
+    for h in range(w.heads):
+        we = O.effective_window(w.windows[h], grid)
+        cost[h] = we[0] * we[1] * we[2]
+    load = [0] * 8
+    for b, code in enumerate(s.tolist()):
+        if code >= 0:
+            h = (code // subs // info.n_tiles) % w.heads
+            load[b % 8] += cost[h]
+    if n_items >= 8 * 32:
+        assert max(load) - min(load) <= 32 * max(cost.values())
+    # decreasing cost along each XCD's queue (list scheduling of an LPT order)
+    for x in range(8):
+        q = [cost[(c // subs // info.n_tiles) % w.heads] for c in s[x::8].tolist() if c >= 0]
+        assert q == sorted(q, reverse=True)
+
+
+def _create(*args):
+    h = ctypes.c_void_p()
+    st = L.lib().sta_plan_create(*args, ctypes.byref(h))
+    if st == L.STA_OK:
+        L.lib().sta_plan_destroy(h)
+    return st
+
+
+def _ints(xs):
+    return (ctypes.c_int * len(xs))(*xs)
+
+
+def test_plan_create_errors():
+    t, w1 = _ints([2, 4, 4]), _ints([3, 3, 3])
+    assert _create(1, 1, 6, 16, 16, t, w1, 64) == L.STA_OK
+    assert _create(1, 1, 7, 16, 16, t, w1, 64) == L.STA_ERR_SHAPE          # 7 % 2
+    assert _create(1, 1, 6, 16, 18, t, w1, 64) == L.STA_ERR_SHAPE
+    assert _create(1, 1, 6, 16, 16, t, w1, 96) == L.STA_ERR_UNSUPPORTED    # head_dim
+    assert _create(1, 1, 6, 16, 16, _ints([1, 2, 2]), w1, 64) == L.STA_ERR_UNSUPPORTED  # 4 tokens/tile
+    assert _create(1, 1, 6, 16, 16, t, _ints([0, 3, 3]), 64) == L.STA_ERR_ARG
+    assert _create(0, 1, 6, 16, 16, t, w1, 64) == L.STA_ERR_ARG
+    assert _create(1, 0, 6, 16, 16, t, w1, 64) == L.STA_ERR_ARG
+    assert _create(1, 1, 6, 16, 16, None, w1, 64) == L.STA_ERR_ARG
+    assert _create(1, 1, 6, 16, 16, t, None, 64) == L.STA_ERR_ARG
+    assert _create(1, 1, 6, 16, 16, _ints([2, 0, 4]), w1, 64) == L.STA_ERR_ARG
+    assert L.lib().sta_plan_create(1, 1, 6, 16, 16, t, w1, 64, None) == L.STA_ERR_ARG
+    assert L.lib().sta_plan_destroy(None) == L.STA_OK
+
+
+def test_plan_query_errors():
+    p = api.Plan(1, 2, (6, 16, 16), (2, 4, 4), [(3, 3, 3)], 64)
+    lib = L.lib()
+    cnt = ctypes.c_int()
+    assert lib.sta_plan_kv_tiles(p.handle, 2, 0, None, 0, ctypes.byref(cnt)) == L.STA_ERR_ARG
+    assert lib.sta_plan_kv_tiles(p.handle, 0, 48, None, 0, ctypes.byref(cnt)) == L.STA_ERR_ARG
+    buf = (ctypes.c_int32 * 4)()
+    assert lib.sta_plan_kv_tiles(p.handle, 0, 0, buf, 4, ctypes.byref(cnt)) == L.STA_ERR_ARG
+    assert cnt.value == 27
+    small = (ctypes.c_int32 * 10)()
+    assert lib.sta_plan_perm(p.handle, small, 10) == L.STA_ERR_ARG
+    n = ctypes.c_int64()
+    assert lib.sta_plan_schedule(p.handle, None, 0, ctypes.byref(n)) == L.STA_ERR_ARG
+    assert n.value == p.info.work_items
+    assert lib.sta_plan_get_info(None, ctypes.byref(L.PlanInfo())) == L.STA_ERR_ARG
+
+
+def test_forward_argument_errors_precede_device_work():
+    # Every check below fails on the host, so no device is needed or touched.
+    p = api.Plan(1, 2, (6, 16, 16), (2, 4, 4), [(3, 3, 3)], 64)
+    lib = L.lib()
+    P = ctypes.c_void_p
+    q, k, v, o = P(1 << 40), P(2 << 40), P(3 << 40), P(4 << 40)
+    assert lib.sta_forward_plan(None, q, k, v, o, 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_forward_plan(p.handle, None, k, v, o, 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_forward_plan(p.handle, q, k, v, None, 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_forward_plan(p.handle, q, k, v, o, 0.0, 0, 1, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_forward_plan(p.handle, q, k, v, o, -1.0, 0, 1, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_forward_plan(p.handle, q, k, v, o, float("nan"), 0, 1, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_forward_plan(p.handle, q, k, v, o, 0.125, 7, 1, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_forward_plan(p.handle, q, k, v, o, 0.125, 0, 7, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_forward_plan(p.handle, q, k, v, o, 0.125, 0, 1, 5, None) == L.STA_ERR_ARG
+    # out overlapping an input
+    assert lib.sta_forward_plan(p.handle, q, k, v, P((1 << 40) + 64), 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_tile_reorder(p.handle, q, P((1 << 40) + 64), 0, None) == L.STA_ERR_ARG
+    assert lib.sta_tile_reorder(None, q, o, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_tile_unreorder(p.handle, q, o, 9, None) == L.STA_ERR_ARG
+    t, win = _ints([2, 4, 4]), _ints([3, 3, 3, 3, 3, 3])
+    assert lib.sta_forward(q, k, v, o, 1, 2, 7, 16, 16, t, win, 64, 0.125, 0, 1, 0, None) == L.STA_ERR_SHAPE
+    assert lib.sta_forward(q, k, v, o, 1, 2, 6, 16, 16, t, win, 80, 0.125, 0, 1, 0, None) == L.STA_ERR_UNSUPPORTED
+    assert lib.sta_forward(q, k, v, o, 1, 2, 6, 16, 16, None, win, 64, 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_clear_plan_cache() == L.STA_OK

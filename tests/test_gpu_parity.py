@@ -1,0 +1,231 @@
+"""GPU parity of the HIP STA forward against the CPU oracle (needs MI355X).
+
+Tolerance (bf16 inputs, fp32 accumulation, fp32 output, against the float64
+oracle fed the very same input values): max |gpu - oracle| <= 2e-2 and
+mean |gpu - oracle| <= 2e-3.  The small workloads are compared on every
+token; the 30x48x80 ones on 64 seeded random query tiles per head plus the
+8 corner tiles (where windows are shifted inward).
+"""
+
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sta_oracle as O
+from sliding_tile_attention_sta_amd import api
+from sliding_tile_attention_sta_amd.synthetic import WORKLOADS, make_qkv, sample_query_tiles
+
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def tile_slice(w, c):
+    tT, tH, tW = w.tile
+    return (slice(c[0] * tT, (c[0] + 1) * tT), slice(c[1] * tH, (c[1] + 1) * tH),
+            slice(c[2] * tW, (c[2] + 1) * tW))
+
+
+def errors(got, want):
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
+    return float(d.max()), float(d.mean())
+
+
+def run_full(w, q, k, v, out_dtype=torch.float32, layout="natural"):
+    plan = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    out = torch.full(q.shape, float("nan"), dtype=out_dtype, device=q.device)
+    api.sta_forward_plan(plan, q, k, v, out=out, scale=w.scale, layout=layout)
+    torch.cuda.synchronize()
+    return plan, out
+
+
+# ---------------------------------------------------------------------------
+# Small workloads: every token
+# ---------------------------------------------------------------------------
+
+def test_tiny_all_tokens():
+    w = WORKLOADS["tiny"]
+    say("case tiny: 6x16x16 tile 2x4x4 w333 2 heads d64 fp32")
+    q, k, v = make_qkv(w)
+    _, out = run_full(w, q.cuda(), k.cuda(), v.cuda())
+    N = w.tokens
+    shp = (1, w.heads, N, w.head_dim)
+    ref = O.sta_forward_explicit(q.reshape(shp).double().numpy(), k.reshape(shp).double().numpy(),
+                                 v.reshape(shp).double().numpy(), w.video, w.tile, w.windows,
+                                 scale=w.scale)
+    got = out.reshape(shp).cpu().numpy()
+    mx, mn = errors(got, ref)
+    say(f"tiny max {mx:.2e} mean {mn:.2e}")
+    assert np.isfinite(got).all()
+    assert mx <= MAX_ABS and mn <= MEAN_ABS
+
+
+def _oracle_tiles(w, q, k, v, head, tiles):
+    """Oracle outputs for the given query tiles of one head (inputs on any device)."""
+    qh, kh, vh = (x[:, head:head + 1].float().cpu().numpy() for x in (q, k, v))
+    return O.sta_forward_query_tiles(qh, kh, vh, w.tile, w.windows[head], 0, tiles, scale=w.scale)
+
+
+def test_small_all_tokens():
+    w = WORKLOADS["small"]
+    say("case small: 12x24x24 tile 6x8x8 w333 8 heads d128 bf16")
+    q, k, v = make_qkv(w)
+    _, out = run_full(w, q.cuda(), k.cuda(), v.cuda())
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    grid = O.tile_grid(w.video, w.tile)
+    tiles = [(a, b, c) for a in range(grid[0]) for b in range(grid[1]) for c in range(grid[2])]
+    worst = (0.0, 0.0)
+    for h in range(w.heads):
+        refs = _oracle_tiles(w, q, k, v, h, tiles)
+        for c, ref in zip(tiles, refs):
+            mx, mn = errors(got[0, h][tile_slice(w, c)], ref)
+            worst = (max(worst[0], mx), max(worst[1], mn))
+            assert mx <= MAX_ABS and mn <= MEAN_ABS, (h, c, mx, mn)
+    say(f"small worst max {worst[0]:.2e} worst tile mean {worst[1]:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: sampled query tiles, in the launch configuration the
+# bench times (natural layout, bf16 in, fp32 out)
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def big_runs():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            w = WORKLOADS[name]
+            q, k, v = make_qkv(w, "cuda")
+            _, out = run_full(w, q, k, v)
+            cache[name] = (w, q, k, v, out)
+        return cache[name]
+
+    yield get
+    cache.clear()
+
+
+@pytest.mark.parametrize("part", [0, 1, 2])
+@pytest.mark.parametrize("name", ["720p", "mixed", "long"])
+def test_large_sampled_tiles(big_runs, name, part):
+    w, q, k, v, out = big_runs(name)
+    heads = [h for h in range(w.heads) if h % 3 == part]
+    say(f"case {name} heads {heads}")
+    t0 = time.time()
+    worst, total_abs, count = 0.0, 0.0, 0
+    for h in heads:
+        tiles = sample_query_tiles(w, h)
+        got_h = out[0, h].cpu().numpy()
+        refs = _oracle_tiles(w, q, k, v, h, tiles)
+        for c, ref in zip(tiles, refs):
+            g = got_h[tile_slice(w, c)]
+            assert np.isfinite(g).all(), (h, c)
+            d = np.abs(g.astype(np.float64) - ref)
+            worst = max(worst, float(d.max()))
+            total_abs += float(d.sum())
+            count += d.size
+            assert float(d.max()) <= MAX_ABS, (h, c, float(d.max()))
+    mean = total_abs / count
+    say(f"{name} part {part}: {count} outputs, max {worst:.2e} mean {mean:.2e} ({time.time() - t0:.0f}s)")
+    assert mean <= MEAN_ABS
+
+
+def test_large_outputs_fully_written(big_runs):
+    # the output was filled with NaN before the call
+    for name in ["720p", "long"]:
+        w, q, k, v, out = big_runs(name)
+        assert not torch.isnan(out).any().item(), name
+
+
+# ---------------------------------------------------------------------------
+# Structure, layout and determinism
+# ---------------------------------------------------------------------------
+
+def _window_readout_inputs(w):
+    """Q = 0, K random, V[token] = (ct, cy, cz, ct^2, cy^2, cz^2, 0, ...): with
+    every weight equal, the output is the mean tile coordinate and mean
+    squared tile coordinate over the key tiles the kernel visited."""
+    T, H, W = w.video
+    t, y, z = torch.meshgrid(torch.arange(T), torch.arange(H), torch.arange(W), indexing="ij")
+    c = [t // w.tile[0], y // w.tile[1], z // w.tile[2]]
+    v = torch.zeros(w.batch, w.heads, T, H, W, w.head_dim)
+    for i in range(3):
+        v[..., i] = c[i].float()
+        v[..., 3 + i] = (c[i] ** 2).float()
+    q = torch.zeros_like(v)
+    k = torch.randn(v.shape, generator=torch.Generator().manual_seed(1))
+    return (x.to(torch.bfloat16).cuda() for x in (q, k, v))
+
+
+@pytest.mark.parametrize("name", ["small", "720p", "mixed"])
+def test_window_readout_matches_golden_geometry(name):
+    w = WORKLOADS[name]
+    if name != "small":
+        w = w.with_heads(4)
+    say(f"case readout {name}")
+    q, k, v = _window_readout_inputs(w)
+    _, out = run_full(w, q, k, v)
+    grid = O.tile_grid(w.video, w.tile)
+    o = out.cpu()
+    for h in range(w.heads):
+        for a in range(grid[0]):
+            for b in range(grid[1]):
+                for cc in range(grid[2]):
+                    rng = O.window_tiles((a, b, cc), w.windows[h], grid)
+                    got = o[0, h][tile_slice(w, (a, b, cc))].reshape(-1, w.head_dim)
+                    for i, (s, e) in enumerate(rng):
+                        idx = np.arange(s, e)
+                        assert torch.allclose(got[:, i], torch.tensor(idx.mean(), dtype=torch.float32), atol=1e-5)
+                        assert torch.allclose(got[:, 3 + i], torch.tensor((idx ** 2).mean(), dtype=torch.float32),
+                                              atol=1e-4)
+                    assert (got[:, 6:] == 0).all()
+
+
+def test_tile_major_layout_and_reorder_roundtrip():
+    w = WORKLOADS["small"]
+    q, k, v = (x.cuda() for x in make_qkv(w))
+    plan, out_nat = run_full(w, q, k, v)
+    # reorder equals a gather with the plan's permutation, bit for bit
+    perm = plan.perm().long().cuda()
+    qt = api.sta_tile_reorder(plan, q)
+    assert torch.equal(qt, q.reshape(1, w.heads, -1, w.head_dim)[:, :, perm])
+    kt, vt = api.sta_tile_reorder(plan, k), api.sta_tile_reorder(plan, v)
+    back = api.sta_tile_unreorder(plan, qt)
+    assert torch.equal(back.reshape(q.shape), q)
+    out_tm = torch.empty(qt.shape, dtype=torch.float32, device="cuda")
+    api.sta_forward_plan(plan, qt, kt, vt, out=out_tm, scale=w.scale, layout="tile_major")
+    out_back = api.sta_tile_unreorder(plan, out_tm)
+    torch.cuda.synchronize()
+    # same arithmetic in the same order: identical bits
+    assert torch.equal(out_back.reshape(out_nat.shape), out_nat)
+
+
+def test_deterministic_and_bf16_output():
+    w = WORKLOADS["small"]
+    q, k, v = (x.cuda() for x in make_qkv(w))
+    _, a = run_full(w, q, k, v)
+    _, b = run_full(w, q, k, v)
+    assert torch.equal(a, b)
+    _, c = run_full(w, q, k, v, out_dtype=torch.bfloat16)
+    assert torch.equal(c, a.to(torch.bfloat16))
+
+
+def test_cached_entry_point_matches_plan_entry_point():
+    w = WORKLOADS["tiny"]
+    q, k, v = (x.cuda() for x in make_qkv(w))
+    _, a = run_full(w, q, k, v)
+    b = api.sta_forward(q, k, v, w.tile, w.windows, scale=w.scale)
+    b2 = api.sta_forward(q, k, v, w.tile, w.windows, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, b2)
