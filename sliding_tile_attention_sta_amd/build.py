@@ -25,6 +25,9 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsta.so")
 
 HIP_SOURCES = ["sta_api.hip", "sta_forward.hip", "sta_reorder.hip"]
+# Per-file extra flags.  The forward kernel needs no IEEE signalling-NaN
+# quieting, which lets v_max_f32 read MFMA results without canonicalising them.
+HIP_EXTRA = {"sta_forward.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 CXX_SOURCES = ["sta_plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")
@@ -52,7 +55,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     cmds, objs = [], []
     for s in HIP_SOURCES:
         o = os.path.join(BUILD, s + ".o")
-        cmds.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
+        cmds.append([HIPCC, *HIP_FLAGS, *HIP_EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o])
         objs.append(o)
     for s in CXX_SOURCES:
         o = os.path.join(BUILD, s + ".o")

@@ -152,6 +152,7 @@ sta_status sta_forward_plan(const sta_plan *p, const void *q, const void *k, con
   a.N = p->N;
   a.sl2e = scale * 1.44269504088896340736f;
   a.n_blocks = (int32_t)p->sched.size();
+  a.max_nkv = p->max_nkv;
   hipError_t e = sta::launch_forward(a, p->variant, p->D, in_dtype == STA_F32, out_dtype == STA_F32,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? STA_OK : STA_ERR_HIP;

@@ -69,41 +69,62 @@ __device__ __forceinline__ float swap_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// 8 consecutive elements at p as bf16 (fp32 inputs are rounded to nearest even).
+// Raw global data of one 8-element chunk (converted when written to LDS, so
+// that the global loads of the next step stay in flight during the math).
+template <bool F32> struct Raw8;
+template <> struct Raw8<false> { uint4 x; };
+template <> struct Raw8<true> { float4 x, y; };
+
 template <bool F32>
-__device__ __forceinline__ uint4 load8(const void *p) {
+__device__ __forceinline__ Raw8<F32> load_raw(const char *p) {
+  Raw8<F32> r;
   if constexpr (F32) {
-    const float4 *f = reinterpret_cast<const float4 *>(p);
-    float4 x = f[0], y = f[1];
-    bf16x8 r;
-    r[0] = (__bf16)x.x; r[1] = (__bf16)x.y; r[2] = (__bf16)x.z; r[3] = (__bf16)x.w;
-    r[4] = (__bf16)y.x; r[5] = (__bf16)y.y; r[6] = (__bf16)y.z; r[7] = (__bf16)y.w;
-    return __builtin_bit_cast(uint4, r);
+    r.x = reinterpret_cast<const float4 *>(p)[0];
+    r.y = reinterpret_cast<const float4 *>(p)[1];
   } else {
-    return *reinterpret_cast<const uint4 *>(p);
+    r.x = *reinterpret_cast<const uint4 *>(p);
+  }
+  return r;
+}
+
+// As bf16 (fp32 inputs rounded to nearest even).
+template <bool F32>
+__device__ __forceinline__ uint4 as_bf16(const Raw8<F32> &r) {
+  if constexpr (F32) {
+    bf16x8 b;
+    b[0] = (__bf16)r.x.x; b[1] = (__bf16)r.x.y; b[2] = (__bf16)r.x.z; b[3] = (__bf16)r.x.w;
+    b[4] = (__bf16)r.y.x; b[5] = (__bf16)r.y.y; b[6] = (__bf16)r.y.z; b[7] = (__bf16)r.y.w;
+    return __builtin_bit_cast(uint4, b);
+  } else {
+    return r.x;
   }
 }
 
-// 8 consecutive elements at p as fp16 for the P.V product.  bf16 values
-// inside the fp16 range convert exactly; magnitudes beyond 65504 saturate
-// (no infinities); fp32 inputs are rounded to nearest even.
+// As fp16 for the P.V product.  bf16 values inside the fp16 range convert
+// exactly; magnitudes beyond 65504 saturate (no infinities); fp32 inputs are
+// rounded to nearest even.
 __device__ __forceinline__ float sat16(float x) { return __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f); }
 
 template <bool F32>
-__device__ __forceinline__ uint4 load8_f16(const void *p) {
-  f16x8 r;
+__device__ __forceinline__ uint4 as_f16(const Raw8<F32> &r) {
+  f16x8 h;
   if constexpr (F32) {
-    const float4 *f = reinterpret_cast<const float4 *>(p);
-    float4 x = f[0], y = f[1];
-    r[0] = (_Float16)sat16(x.x); r[1] = (_Float16)sat16(x.y); r[2] = (_Float16)sat16(x.z); r[3] = (_Float16)sat16(x.w);
-    r[4] = (_Float16)sat16(y.x); r[5] = (_Float16)sat16(y.y); r[6] = (_Float16)sat16(y.z); r[7] = (_Float16)sat16(y.w);
+    h[0] = (_Float16)sat16(r.x.x); h[1] = (_Float16)sat16(r.x.y);
+    h[2] = (_Float16)sat16(r.x.z); h[3] = (_Float16)sat16(r.x.w);
+    h[4] = (_Float16)sat16(r.y.x); h[5] = (_Float16)sat16(r.y.y);
+    h[6] = (_Float16)sat16(r.y.z); h[7] = (_Float16)sat16(r.y.w);
   } else {
-    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(p);
+    const bf16x8 b = __builtin_bit_cast(bf16x8, r.x);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (_Float16)sat16((float)b[i]);
+    for (int i = 0; i < 8; ++i) h[i] = (_Float16)sat16((float)b[i]);
   }
-  return __builtin_bit_cast(uint4, r);
+  return __builtin_bit_cast(uint4, h);
 }
+
+// Lazy rescaling: the running reference max only moves when a block's max
+// exceeds it by more than 2^kTau in exp2 units, so probabilities stay
+// <= 2^kTau (comfortably inside fp16) and O is rarely rescaled.
+constexpr float kTau = 8.f;
 
 // D: head dim.  QB: 16-query blocks per wave.  NW: waves per group.
 template <int D, int QB, int NW, bool F32IN, bool F32OUT>
@@ -121,7 +142,10 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   constexpr int DC = D / 32;                      // 32-wide d chunks (QK^T K-dim steps)
   constexpr int DB = D / 16;                      // 16-wide d blocks (rows of O^T)
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * KST_BYTES + 2 * VST_BYTES];
+  // LDS: K stages, V stages, tile-local row offsets, key-tile base rows.
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int *off_l = reinterpret_cast<int *>(smem + 2 * KST_BYTES + 2 * VST_BYTES);
+  int *kvb_l = off_l + a.V;
 
   const int item = a.sched[blockIdx.x];
   if (item < 0) return;
@@ -137,43 +161,51 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   const int l16 = lane & 15;
   const int g = lane >> 4;
 
+  // Work-item constants are wave-uniform; readfirstlane keeps them in SGPRs
+  // so that the key loop is a scalar (non-divergent) loop.
+  const int kv0 = __builtin_amdgcn_readfirstlane(a.kv_off[h * a.n_tiles + qt]);
+  const int nkv = __builtin_amdgcn_readfirstlane(a.kv_off[h * a.n_tiles + qt + 1]) - kv0;
+  for (int i = tid; i < a.V; i += NT) off_l[i] = a.off[i];
+  for (int i = tid; i < nkv; i += NT) kvb_l[i] = a.base[a.kv_idx[kv0 + i]];
+
   const char *qg = reinterpret_cast<const char *>(a.q) + (size_t)bh * a.N * D * EB;
   const char *kg = reinterpret_cast<const char *>(a.k) + (size_t)bh * a.N * D * EB;
   const char *vg = reinterpret_cast<const char *>(a.v) + (size_t)bh * a.N * D * EB;
+  const int qbase = a.base[qt];
+  const int qloc0 = sub * QPI + wave * 16 * QB;
+  __syncthreads();
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in VGPRs --------------
   bf16x8 qf[QB][DC];
-  const int qbase = a.base[qt];
-  const int qloc0 = sub * QPI + wave * 16 * QB;
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    const int row = qbase + a.off[qloc0 + 16 * j + l16];
+    const int row = qbase + off_l[qloc0 + 16 * j + l16];
 #pragma unroll
     for (int c = 0; c < DC; ++c)
-      qf[j][c] = __builtin_bit_cast(bf16x8, load8<F32IN>(qg + ((size_t)row * D + 32 * c + 8 * g) * EB));
+      qf[j][c] = __builtin_bit_cast(bf16x8, as_bf16<F32IN>(load_raw<F32IN>(
+                                              qg + ((size_t)row * D + 32 * c + 8 * g) * EB)));
   }
 
   // ---- key-tile walk ------------------------------------------------------
-  const int kv0 = a.kv_off[h * a.n_tiles + qt];
-  const int nkv = a.kv_off[h * a.n_tiles + qt + 1] - kv0;
-  const int steps_per_tile = a.V / KB;
-  const int nsteps = nkv * steps_per_tile;
+  const int spt = a.V / KB;        // steps per key tile
+  const int nsteps = nkv * spt;
 
-  uint4 pk[CPT], pv[CPT];
-  auto fetch = [&](int s) {
-    const int tile = a.kv_idx[kv0 + s / steps_per_tile];
-    const int loc0 = (s % steps_per_tile) * KB;
-    const int tb = a.base[tile];
+  Raw8<F32IN> pk[CPT], pv[CPT];
+  int f_ti = 0, f_u = 0;           // key tile and step-in-tile of the next fetch
+  auto fetch = [&]() {
+    const int tb = kvb_l[f_ti];
+    const int loc0 = f_u * KB;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (CHUNKS < NT && c >= CHUNKS) break;
       const int r = c / (D / 8);
       const int col = (c % (D / 8)) * 8;
-      const size_t e = (size_t)(tb + a.off[loc0 + r]) * D + col;
-      pk[i] = load8<F32IN>(kg + e * EB);
-      pv[i] = load8_f16<F32IN>(vg + e * EB);
+      const size_t e = (size_t)(tb + off_l[loc0 + r]) * D + col;
+      pk[i] = load_raw<F32IN>(kg + e * EB);
+      pv[i] = load_raw<F32IN>(vg + e * EB);
     }
+    if (++f_u == spt) { f_u = 0; ++f_ti; }
   };
   auto stash = [&](int stage) {
     char *ks = smem + stage * KST_BYTES;
@@ -184,8 +216,8 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
       if (CHUNKS < NT && c >= CHUNKS) break;
       const int r = c / (D / 8);
       const int col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4 *>(ks + r * KSTR + col * 2) = pk[i];
-      *reinterpret_cast<uint4 *>(vs + r * VSTR + col * 2) = pv[i];
+      *reinterpret_cast<uint4 *>(ks + r * KSTR + col * 2) = as_bf16<F32IN>(pk[i]);
+      *reinterpret_cast<uint4 *>(vs + r * VSTR + col * 2) = as_f16<F32IN>(pv[i]);
     }
   };
 
@@ -200,13 +232,17 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   }
   const float sl2e = a.sl2e;
 
-  fetch(0);
+  fetch();
   stash(0);
   __syncthreads();
+  // Retire every outstanding load (the Q fragments included) before the
+  // loop, so that inside it the only vector-memory wait is the one for the
+  // prefetched K/V block at the LDS write.
+  __builtin_amdgcn_s_waitcnt(0);
 
   for (int s = 0; s < nsteps; ++s) {
     const int stage = s & 1;
-    if (s + 1 < nsteps) fetch(s + 1);
+    if (s + 1 < nsteps) fetch();
     const char *ks = smem + stage * KST_BYTES;
     const char *vs = smem + 2 * KST_BYTES + stage * VST_BYTES;
 
@@ -232,22 +268,24 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
       float mx = fmaxf(fmaxf(fmaxf(st[0][j][0], st[0][j][1]), fmaxf(st[0][j][2], st[0][j][3])),
                        fmaxf(fmaxf(st[1][j][0], st[1][j][1]), fmaxf(st[1][j][2], st[1][j][3])));
       mx = swap_max(mx);
-      const float mnew = fmaxf(m[j], mx);
-      const float alpha = __builtin_amdgcn_exp2f((m[j] - mnew) * sl2e);
-      m[j] = mnew;
-      const float mb = mnew * sl2e;
-      float ps = 0.f;
+      if (__builtin_amdgcn_ballot_w64((mx - m[j]) * sl2e > kTau)) {
+        const float mnew = fmaxf(m[j], mx);
+        const float alpha = __builtin_amdgcn_exp2f((m[j] - mnew) * sl2e);
+        m[j] = mnew;
+        l[j] *= alpha;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) o[b][j] *= alpha;
+      }
+      const float mb = m[j] * sl2e;
+      float p[8];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r], sl2e, -mb));
-          ps += p;
-          pb[j][kb * 4 + r] = (_Float16)p;
+          p[kb * 4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r], sl2e, -mb));
+          pb[j][kb * 4 + r] = (_Float16)p[kb * 4 + r];
         }
-      l[j] = l[j] * alpha + ps;
-#pragma unroll
-      for (int b = 0; b < DB; ++b) o[b][j] *= alpha;
+      l[j] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     }
 
     // O^T[d][query] += V^T P^T.
@@ -275,7 +313,7 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     const float inv = 1.f / swap_sum(l[j]);
-    const int row = qbase + a.off[qloc0 + 16 * j + l16];
+    const int row = qbase + off_l[qloc0 + 16 * j + l16];
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       const f32x4 r = o[b][j] * inv;
@@ -292,16 +330,26 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
 }
 
 template <int D, int QB, int NW>
-hipError_t launch_io(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s) {
-  dim3 grid(a.n_blocks), block(NW * 64);
-  if (f32_in) {
-    if (f32_out) hipLaunchKernelGGL((sta_fwd_kernel<D, QB, NW, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((sta_fwd_kernel<D, QB, NW, true, false>), grid, block, 0, s, a);
-  } else {
-    if (f32_out) hipLaunchKernelGGL((sta_fwd_kernel<D, QB, NW, false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((sta_fwd_kernel<D, QB, NW, false, false>), grid, block, 0, s, a);
+constexpr size_t stage_bytes() { return 2 * (size_t)KB * (D * 2 + 16) * 2; }
+
+template <int D, int QB, int NW, bool FI, bool FO>
+hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
+  auto kern = sta_fwd_kernel<D, QB, NW, FI, FO>;
+  const size_t lds = stage_bytes<D, QB, NW>() + sizeof(int) * ((size_t)a.V + a.max_nkv);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
   }
+  hipLaunchKernelGGL(kern, dim3(a.n_blocks), dim3(NW * 64), lds, s, a);
   return hipGetLastError();
+}
+
+template <int D, int QB, int NW>
+hipError_t launch_io(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s) {
+  if (f32_in) return f32_out ? launch_one<D, QB, NW, true, true>(a, s) : launch_one<D, QB, NW, true, false>(a, s);
+  return f32_out ? launch_one<D, QB, NW, false, true>(a, s) : launch_one<D, QB, NW, false, false>(a, s);
 }
 
 }  // namespace

@@ -47,6 +47,7 @@ struct sta_plan {
   std::vector<int32_t> sched;     // launch order of work items, -1 = idle
   std::vector<int32_t> base_nat, off_nat;
   int64_t pairs = 0;
+  int32_t max_nkv = 0;    // longest key-tile list
   int32_t variant = 0;
   int32_t qpi = 0;        // queries per work item
   int32_t subs = 0;       // work items per (b, head, query tile)

@@ -19,6 +19,7 @@ struct FwdArgs {
   int64_t N;               // tokens per (batch, head)
   float sl2e;              // softmax scale * log2(e)
   int32_t n_blocks;        // length of sched
+  int32_t max_nkv;         // longest key-tile list of any (head, query tile)
 };
 
 // Launch the forward kernel.  variant: 0 generic, 1 384-query items.

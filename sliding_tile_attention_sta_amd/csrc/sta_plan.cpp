@@ -128,6 +128,15 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
       }
     }
     p->pairs = (int64_t)p->kv_idx.size();
+    for (size_t i = 0; i + 1 < p->kv_off.size(); ++i)
+      p->max_nkv = std::max(p->max_nkv, p->kv_off[i + 1] - p->kv_off[i]);
+    // The forward kernel keeps two K and two V stages of 32 keys plus the
+    // tile-local row offsets and the item's key-tile rows in LDS (160 KiB).
+    const int64_t lds = 2LL * kKeyBlock * (2 * head_dim + 16) * 2 + 4LL * (p->V + p->max_nkv);
+    if (lds > 160 * 1024) {
+      delete p;
+      return STA_ERR_UNSUPPORTED;
+    }
 
     // Token row tables for the natural layout.
     p->base_nat.resize(p->n_tiles);
