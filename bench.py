@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--workload", default="720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (4 times); "
+                         "used to calibrate HBM traffic counters")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                            "profiles", "traffic.json"))
     return ap.parse_args()
@@ -118,6 +121,16 @@ def main():
     import torch
     from sliding_tile_attention_sta_amd import api
     from sliding_tile_attention_sta_amd.synthetic import WORKLOADS, make_qkv
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(4):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "launches": 4}))
+        return
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

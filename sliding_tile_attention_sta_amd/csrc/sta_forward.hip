@@ -29,8 +29,10 @@
 //     row-major V in LDS with ds_read_b64_tr_b16, which transposes 4x16
 //     16-bit blocks inside each 16-lane group, so V is never transposed in
 //     memory.
-//   * K and V advance 32 keys at a time through a two-stage LDS ring; the
-//     next block's global loads are issued before the current block's math.
+//   * K and V advance 32 keys at a time through two-stage LDS rings; the
+//     next blocks' global loads are issued before the current block's math.
+//   * The two waves sharing a SIMD run half a step apart (ping-pong), so
+//     one wave's softmax VALU work overlaps the other's MFMAs.
 //   * Rows are located through two small tables (tile base row, tile-local
 //     row offset), so one kernel reads and writes either the natural
 //     [T, H, W] token order or the tile-major order.
@@ -38,7 +40,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
+#include "sta_internal.h"
 #include "sta_launch.h"
 
 namespace sta {
@@ -53,7 +57,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int KB = 32;  // keys per pipeline step
+constexpr int KB = kKeyBlock;  // keys per pipeline step
 
 __device__ __forceinline__ float swap_max(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -131,8 +135,8 @@ template <int D, int QB, int NW, bool F32IN, bool F32OUT>
 __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QPI = 16 * QB * NW;               // queries per work item
-  constexpr int KSTR = D * 2 + 16;                // LDS row stride (bytes), padded
-  constexpr int VSTR = D * 2 + 16;
+  constexpr int KSTR = fwd_kstride(D);            // padded LDS row strides (bytes)
+  constexpr int VSTR = fwd_vstride(D);
   constexpr int KST_BYTES = KB * KSTR;
   constexpr int VST_BYTES = KB * VSTR;
   constexpr int CHUNKS = KB * D / 8;              // 8-element chunks per tensor per step
@@ -190,34 +194,38 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   const int spt = a.V / KB;        // steps per key tile
   const int nsteps = nkv * spt;
 
-  Raw8<F32IN> pk[CPT], pv[CPT];
-  int f_ti = 0, f_u = 0;           // key tile and step-in-tile of the next fetch
-  auto fetch = [&]() {
-    const int tb = kvb_l[f_ti];
-    const int loc0 = f_u * KB;
+  // Global -> register prefetch of one 32-key block of K and of V.
+  Raw8<F32IN> rk[CPT], rv[CPT];
+  int fk_ti = 0, fk_u = 0, fv_ti = 0, fv_u = 0;   // key tile / step-in-tile of the next fetch
+  auto fetch = [&](Raw8<F32IN>(&dst)[CPT], const char *src, int &ti, int &u) {
+    const int tb = kvb_l[ti];
+    const int loc0 = u * KB;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (CHUNKS < NT && c >= CHUNKS) break;
       const int r = c / (D / 8);
       const int col = (c % (D / 8)) * 8;
-      const size_t e = (size_t)(tb + off_l[loc0 + r]) * D + col;
-      pk[i] = load_raw<F32IN>(kg + e * EB);
-      pv[i] = load_raw<F32IN>(vg + e * EB);
+      dst[i] = load_raw<F32IN>(src + ((size_t)(tb + off_l[loc0 + r]) * D + col) * EB);
     }
-    if (++f_u == spt) { f_u = 0; ++f_ti; }
+    if (++u == spt) { u = 0; ++ti; }
   };
-  auto stash = [&](int stage) {
+  auto stash_k = [&](const Raw8<F32IN>(&src)[CPT], int stage) {
     char *ks = smem + stage * KST_BYTES;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS < NT && c >= CHUNKS) break;
+      *reinterpret_cast<uint4 *>(ks + (c / (D / 8)) * KSTR + (c % (D / 8)) * 16) = as_bf16<F32IN>(src[i]);
+    }
+  };
+  auto stash_v = [&](const Raw8<F32IN>(&src)[CPT], int stage) {
     char *vs = smem + 2 * KST_BYTES + stage * VST_BYTES;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (CHUNKS < NT && c >= CHUNKS) break;
-      const int r = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4 *>(ks + r * KSTR + col * 2) = as_bf16<F32IN>(pk[i]);
-      *reinterpret_cast<uint4 *>(vs + r * VSTR + col * 2) = as_f16<F32IN>(pv[i]);
+      *reinterpret_cast<uint4 *>(vs + (c / (D / 8)) * VSTR + (c % (D / 8)) * 16) = as_f16<F32IN>(src[i]);
     }
   };
 
@@ -231,23 +239,12 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     for (int b = 0; b < DB; ++b) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sl2e = a.sl2e;
+  f32x4 st[2][QB];   // S^T of the current block
+  f16x8 pb[QB];      // its probabilities, fp16
 
-  fetch();
-  stash(0);
-  __syncthreads();
-  // Retire every outstanding load (the Q fragments included) before the
-  // loop, so that inside it the only vector-memory wait is the one for the
-  // prefetched K/V block at the LDS write.
-  __builtin_amdgcn_s_waitcnt(0);
-
-  for (int s = 0; s < nsteps; ++s) {
-    const int stage = s & 1;
-    if (s + 1 < nsteps) fetch();
+  // S^T[key][query] = K Q^T for 32 keys (two 16-key blocks) x 16*QB queries.
+  auto qk = [&](int stage) {
     const char *ks = smem + stage * KST_BYTES;
-    const char *vs = smem + 2 * KST_BYTES + stage * VST_BYTES;
-
-    // S^T[key][query] for 32 keys (two 16-key blocks) x 16*QB queries.
-    f32x4 st[2][QB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -260,9 +257,10 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
           st[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[j][c], st[kb][j], 0, 0, 0);
       }
     }
+  };
 
-    // Online softmax; lane holds query 16j + l16, keys 4g + r and 16 + 4g + r.
-    f16x8 pb[QB];
+  // Online softmax; lane holds query 16j + l16, keys 4g + r and 16 + 4g + r.
+  auto softmax = [&]() {
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       float mx = fmaxf(fmaxf(fmaxf(st[0][j][0], st[0][j][1]), fmaxf(st[0][j][2], st[0][j][3])),
@@ -287,10 +285,13 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
         }
       l[j] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     }
+  };
 
-    // O^T[d][query] += V^T P^T.
-    const int trow = 4 * g + (l16 >> 2);
-    const int tcol = 4 * (l16 & 3);
+  // O^T[d][query] += V^T P^T.
+  const int trow = 4 * g + (l16 >> 2);
+  const int tcol = 4 * (l16 & 3);
+  auto pvmm = [&](int stage) {
+    const char *vs = smem + 2 * KST_BYTES + stage * VST_BYTES;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       const lds_char *vb = (const lds_char *)(vs) + b * 32 + tcol * 2;
@@ -303,10 +304,53 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < QB; ++j) o[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[j], o[b][j], 0, 0, 0);
     }
+  };
 
-    if (s + 1 < nsteps) stash(stage ^ 1);
+  // Ping-pong: the group's two halves run half a step apart.  Waves w and
+  // w + NW/2 share a SIMD, so while one issues the MFMAs of PV(s-1) and
+  // QK(s) the other runs the softmax VALU work, and the two overlap.
+  //   half 0: group A  PV(s-1), QK(s)      group B  softmax(s-1)
+  //   half 1: group A  softmax(s)          group B  PV(s-1), QK(s)
+  // LDS holds K(s) and V(s-1) during step s.  Block s = (K(s+1), V(s)) is
+  // loaded into registers at the start of step s and written into the other
+  // LDS stages at its end.  (Measured on MI355X: this beat both a per-group
+  // write inside the softmax half and a one-step-deeper register prefetch.)
+  const bool grp_a = wave < NW / 2;
+  fetch(rk, kg, fk_ti, fk_u);               // K(0), all threads
+  stash_k(rk, 0);
+  auto fetch_block = [&](int b) {
+    if (b + 1 < nsteps) fetch(rk, kg, fk_ti, fk_u);
+    fetch(rv, vg, fv_ti, fv_u);
+  };
+  fetch_block(0);
+  __syncthreads();
+  // Retire every outstanding load (the Q fragments included) before the
+  // loop, so that inside it the only vector-memory waits are the ones for
+  // the prefetched K/V blocks at their LDS writes.
+  __builtin_amdgcn_s_waitcnt(0);
+
+  for (int s = 0; s < nsteps; ++s) {
+    const bool more = s + 1 < nsteps;
+    if (s > 0) fetch_block(s);
+    if (grp_a) {
+      if (s > 0) pvmm((s - 1) & 1);
+      qk(s & 1);
+    } else if (s > 0) {
+      softmax();
+    }
+    __syncthreads();
+    if (grp_a) {
+      softmax();
+    } else {
+      if (s > 0) pvmm((s - 1) & 1);
+      qk(s & 1);
+    }
+    if (more) stash_k(rk, (s + 1) & 1);
+    stash_v(rv, s & 1);
     __syncthreads();
   }
+  if (!grp_a) softmax();
+  pvmm((nsteps - 1) & 1);
 
   // ---- finalize: O = O^T / l, stored row-major ----------------------------
   char *og = reinterpret_cast<char *>(a.o) + (size_t)bh * a.N * D * (F32OUT ? 4 : 2);
@@ -329,13 +373,11 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int QB, int NW>
-constexpr size_t stage_bytes() { return 2 * (size_t)KB * (D * 2 + 16) * 2; }
 
 template <int D, int QB, int NW, bool FI, bool FO>
 hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
   auto kern = sta_fwd_kernel<D, QB, NW, FI, FO>;
-  const size_t lds = stage_bytes<D, QB, NW>() + sizeof(int) * ((size_t)a.V + a.max_nkv);
+  const size_t lds = (size_t)fwd_stage_bytes(D) + sizeof(int) * ((size_t)a.V + a.max_nkv);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),

@@ -21,6 +21,19 @@ constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, blocks 
 constexpr int kKeyBlock = 32;     // keys staged in LDS per pipeline step
 constexpr int kMaxTileTokens = 4096;
 
+// LDS row strides of the forward kernel's K and V stages (bytes), padded so
+// that the MFMA operand reads avoid bank conflicts.  Measured on gfx950 with
+// the kernel's own access patterns (16 rows x 16 B per 16-lane group for K,
+// 4 rows x 32 B per group for the transposing V reads): a 32-byte pad gives
+// the highest LDS throughput for both (154 and 176 B/clk/CU against 111 and
+// 129 with a 16-byte pad, 29 and 36 unpadded).
+constexpr int fwd_kstride(int head_dim) { return 2 * head_dim + 32; }
+constexpr int fwd_vstride(int head_dim) { return 2 * head_dim + 32; }
+// Two K stages and two V stages of kKeyBlock keys.
+constexpr long long fwd_stage_bytes(int head_dim) {
+  return 2LL * kKeyBlock * (fwd_kstride(head_dim) + fwd_vstride(head_dim));
+}
+
 struct DeviceTables {
   int32_t *kv_off = nullptr;       // heads*n_tiles + 1
   int32_t *kv_idx = nullptr;       // sum of list lengths
