@@ -17,6 +17,7 @@ unreorder path, and the same kernel with a full window (dense attention).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -149,17 +150,25 @@ def main():
 
     # The step is a single launch of the forward kernel on `stream`, so the
     # per-launch kernel duration is the event time per step.
+    # HBM traffic per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    # measurement, used only while the kernel source is the one measured.
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
             with open(args.traffic_json) as f:
                 t = json.load(f)
-            if t.get("workload") == w.name:
+            src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sliding_tile_attention_sta_amd",
+                               "csrc", "sta_forward.hip")
+            with open(src, "rb") as f:
+                digest = hashlib.sha256(f.read()).hexdigest()
+            if t.get("workload") == w.name and t.get("kernel_source_sha256") == digest:
                 traffic = t.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch (HBM, FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "algorithmic_flops_per_launch": flops,
                 "kernel": "sta_fwd_kernel<128,3,8,bf16 in,f32 out>"}
 
     result = {

@@ -421,3 +421,16 @@ def test_pins_catch_planted_mistake(tag, old, new):
         src = f.read()
     mod = _mutant(src, old, new, tag)
     assert run_pins(mod) != [], f"mutant '{tag}' survived every pin"
+
+
+def test_token_predicate_matches_bruteforce():
+    # the scalar predicate `permitted` against the brute-force key lists
+    rng = np.random.default_rng(21)
+    for _ in range(4):
+        video, tile, windows = rand_case(rng, max_tokens=96)
+        grid = O.tile_grid(video, tile)
+        coords = O.natural_coords(video)
+        for n in range(0, len(coords), 3):
+            want = set(bf_keys(tuple(coords[n]), video, tile, windows[0]))
+            got = {j for j in range(len(coords)) if O.permitted(coords[n], coords[j], tile, windows[0], grid)}
+            assert got == want
