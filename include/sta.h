@@ -118,12 +118,15 @@ sta_status sta_tile_reorder(const sta_plan *plan, const void *in, void *out, sta
 sta_status sta_tile_unreorder(const sta_plan *plan, const void *in, void *out, sta_dtype dtype,
                               void *stream);
 
-/* STA forward with a plan.  q, k, v: [batch, heads, N, head_dim] of in_dtype
- * (STA_F32 inputs are rounded to bf16, nearest-even, as they are loaded);
+/* STA forward with a plan.  q, k, v: [batch, heads, N, head_dim] of in_dtype;
  * out: same shape, out_dtype (STA_F32 or STA_BF16).  All four tensors use the
  * token order given by layout.  scale > 0 multiplies Q.K (usually
- * 1/sqrt(head_dim)).  Products run on bf16 MFMA with fp32 accumulation; the
- * softmax runs in fp32. */
+ * 1/sqrt(head_dim)).
+ * Precision: Q.K^T runs on bf16 MFMA (STA_F32 q and k are rounded to bf16,
+ * nearest-even, as they are loaded); the softmax runs in fp32; P.V runs on
+ * fp16 MFMA with P rounded to fp16 and V converted to fp16 (exact for bf16
+ * values, nearest-even for fp32), all accumulated in fp32.  V must lie
+ * within the fp16 range, |v| <= 65504: larger entries become infinities. */
 sta_status sta_forward_plan(const sta_plan *plan, const void *q, const void *k, const void *v,
                             void *out, float scale, sta_dtype in_dtype, sta_dtype out_dtype,
                             sta_layout layout, void *stream);
