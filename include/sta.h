@@ -126,7 +126,9 @@ sta_status sta_tile_unreorder(const sta_plan *plan, const void *in, void *out, s
  * nearest-even, as they are loaded); the softmax runs in fp32; P.V runs on
  * fp16 MFMA with P rounded to fp16 and V converted to fp16 (exact for bf16
  * values, nearest-even for fp32), all accumulated in fp32.  V must lie
- * within the fp16 range, |v| <= 65504: larger entries become infinities. */
+ * within the fp16 range, |v| <= 65504: larger entries become infinities.
+ * Inputs must be finite.  The result does not depend on the order in which
+ * key tiles are visited beyond fp32 rounding. */
 sta_status sta_forward_plan(const sta_plan *plan, const void *q, const void *k, const void *v,
                             void *out, float scale, sta_dtype in_dtype, sta_dtype out_dtype,
                             sta_layout layout, void *stream);

@@ -7,28 +7,35 @@
 // either fully attended or skipped, the kernel never evaluates a mask: it
 // walks the key-tile list of its query tile and runs dense blocks.  The
 // summary page credits the original kernel's speed to dense computation on
-// the sparse pattern in the FlashAttention line (online softmax over
-// streamed key blocks); this kernel keeps that idea and is otherwise laid
-// out for CDNA4:
+// the sparse pattern in the FlashAttention line (softmax over streamed key
+// blocks); this kernel keeps that idea and is otherwise laid out for CDNA4:
 //
 //   * One work group owns QPI query tokens of one (batch, head, query tile)
 //     and keeps them for the whole window; each wave owns 16*QB queries.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_16x16x32_bf16: K comes from LDS, Q stays in VGPRs.  In the
 //     accumulator layout a lane holds one query and 4 keys of each 16x16
-//     block, so the row max and row sum are in-lane reductions plus two
-//     lane swaps (v_permlane16_swap, v_permlane32_swap).
-//   * The softmax is online, in fp32, with exp2 and the scale folded into
-//     one FMA; probabilities (in [0, 1]) are rounded to fp16, nearest even,
-//     straight into the B operand of the second product.  fp16 keeps 11
-//     significant bits against bf16's 8, which cuts the error of the
-//     weighted sum about tenfold when a few keys dominate a row.
+//     block.
+//   * Softmax in fp32 with exp2 and the scale folded into one FMA, against
+//     one reference max per query row for the whole walk: the accumulators
+//     are never rescaled and a step computes no row max, which takes about a
+//     fifth of the VALU work off the step (the kernel is bound by VALU issue,
+//     not by the MFMAs).  The first attempt takes each row's max over the
+//     first key block.  Later blocks may exceed it; probabilities are rounded
+//     to fp16 (nearest even), which holds values up to 65504, and one that
+//     overflows becomes +inf, and so does its row sum.  A work group that
+//     finds a non-finite row sum at the end computes the exact row maxima with
+//     a pass of S^T only (bitwise the same scores) and walks again, now with
+//     every probability <= 1.  For ordinary inputs the first block's max lies
+//     within a few units of the row max and the second walk never runs.
+//   * fp16 keeps 11 significant bits against bf16's 8, which cuts the error
+//     of the weighted sum about tenfold when a few keys dominate a row.  The
+//     row sum is accumulated from the rounded probabilities with
+//     v_dot2_f32_f16, so numerator and denominator use the same values.
 //   * O^T += V^T P^T on v_mfma_f32_16x16x32_f16.  V is converted to fp16 as
-//     it is staged into LDS (exact for bf16 values up to 65504 in
-//     magnitude; larger ones saturate).  The V^T operand is read from
-//     row-major V in LDS with ds_read_b64_tr_b16, which transposes 4x16
-//     16-bit blocks inside each 16-lane group, so V is never transposed in
-//     memory.
+//     it is staged into LDS.  The V^T operand is read from row-major V in LDS
+//     with ds_read_b64_tr_b16, which transposes 4x16 16-bit blocks inside
+//     each 16-lane group, so V is never transposed in memory.
 //   * K and V advance 32 keys at a time through two-stage LDS rings; the
 //     next blocks' global loads are issued before the current block's math.
 //   * The two waves sharing a SIMD run each step in opposite orders
@@ -40,25 +47,17 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <type_traits>
 
+#include "sta_device.h"
 #include "sta_internal.h"
 #include "sta_launch.h"
 
 namespace sta {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) char lds_char;
-
 constexpr int KB = kKeyBlock;  // keys per pipeline step
 
+// Max / sum of x over the four 16-lane groups (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float swap_max(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -72,63 +71,6 @@ __device__ __forceinline__ float swap_sum(float x) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
-
-// Raw global data of one 8-element chunk (converted when written to LDS, so
-// that the global loads of the next step stay in flight during the math).
-template <bool F32> struct Raw8;
-template <> struct Raw8<false> { uint4 x; };
-template <> struct Raw8<true> { float4 x, y; };
-
-template <bool F32>
-__device__ __forceinline__ Raw8<F32> load_raw(const char *p) {
-  Raw8<F32> r;
-  if constexpr (F32) {
-    r.x = reinterpret_cast<const float4 *>(p)[0];
-    r.y = reinterpret_cast<const float4 *>(p)[1];
-  } else {
-    r.x = *reinterpret_cast<const uint4 *>(p);
-  }
-  return r;
-}
-
-// As bf16 (fp32 inputs rounded to nearest even).
-template <bool F32>
-__device__ __forceinline__ uint4 as_bf16(const Raw8<F32> &r) {
-  if constexpr (F32) {
-    bf16x8 b;
-    b[0] = (__bf16)r.x.x; b[1] = (__bf16)r.x.y; b[2] = (__bf16)r.x.z; b[3] = (__bf16)r.x.w;
-    b[4] = (__bf16)r.y.x; b[5] = (__bf16)r.y.y; b[6] = (__bf16)r.y.z; b[7] = (__bf16)r.y.w;
-    return __builtin_bit_cast(uint4, b);
-  } else {
-    return r.x;
-  }
-}
-
-// As fp16 for the P.V product.  bf16 values inside the fp16 range convert
-// exactly; fp32 inputs are rounded to nearest even.  The caller keeps V within
-// the fp16 range (|v| <= 65504); a saturating clamp here sits on the step's
-// critical path and costs about 3 % on MI355X.
-
-template <bool F32>
-__device__ __forceinline__ uint4 as_f16(const Raw8<F32> &r) {
-  f16x8 h;
-  if constexpr (F32) {
-    h[0] = (_Float16)(r.x.x); h[1] = (_Float16)(r.x.y);
-    h[2] = (_Float16)(r.x.z); h[3] = (_Float16)(r.x.w);
-    h[4] = (_Float16)(r.y.x); h[5] = (_Float16)(r.y.y);
-    h[6] = (_Float16)(r.y.z); h[7] = (_Float16)(r.y.w);
-  } else {
-    const bf16x8 b = __builtin_bit_cast(bf16x8, r.x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = (_Float16)((float)b[i]);
-  }
-  return __builtin_bit_cast(uint4, h);
-}
-
-// Lazy rescaling: the running reference max only moves when a block's max
-// exceeds it by more than 2^kTau in exp2 units, so probabilities stay
-// <= 2^kTau (comfortably inside fp16) and O is rarely rescaled.
-constexpr float kTau = 8.f;
 
 // D: head dim.  QB: 16-query blocks per wave.  NW: waves per group.
 template <int D, int QB, int NW, bool F32IN, bool F32OUT>
@@ -146,9 +88,11 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   constexpr int DC = D / 32;                      // 32-wide d chunks (QK^T K-dim steps)
   constexpr int DB = D / 16;                      // 16-wide d blocks (rows of O^T)
 
-  // LDS: K stages, V stages, tile-local row offsets, key-tile base rows.
+  // LDS: K stages, V stages, a flag word (16 bytes), tile-local row
+  // offsets, key-tile base rows.
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  int *off_l = reinterpret_cast<int *>(smem + 2 * KST_BYTES + 2 * VST_BYTES);
+  int *flag_l = reinterpret_cast<int *>(smem + 2 * KST_BYTES + 2 * VST_BYTES);
+  int *off_l = flag_l + 4;
   int *kvb_l = off_l + a.V;
 
   const int item = a.sched[blockIdx.x];
@@ -240,13 +184,6 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
 
   f32x4 o[DB][QB];
   float m[QB], l[QB];
-#pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
-#pragma unroll
-    for (int b = 0; b < DB; ++b) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
   const float sl2e = a.sl2e;
   f32x4 st[2][QB];   // S^T of the current block
   f16x8 pb[QB];      // its probabilities, fp16
@@ -268,32 +205,29 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // Online softmax; lane holds query 16j + l16, keys 4g + r and 16 + 4g + r.
+  // Softmax against the fixed reference: lane holds query 16j + l16, keys
+  // 4g + r and 16 + 4g + r.  l is the lane's partial row sum.
+  float mb[QB];      // reference max * scale * log2(e)
   auto softmax = [&]() {
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
-      float mx = fmaxf(fmaxf(fmaxf(st[0][j][0], st[0][j][1]), fmaxf(st[0][j][2], st[0][j][3])),
-                       fmaxf(fmaxf(st[1][j][0], st[1][j][1]), fmaxf(st[1][j][2], st[1][j][3])));
-      mx = swap_max(mx);
-      if (__builtin_amdgcn_ballot_w64((mx - m[j]) * sl2e > kTau)) {
-        const float mnew = fmaxf(m[j], mx);
-        const float alpha = __builtin_amdgcn_exp2f((m[j] - mnew) * sl2e);
-        m[j] = mnew;
-        l[j] *= alpha;
-#pragma unroll
-        for (int b = 0; b < DB; ++b) o[b][j] *= alpha;
-      }
-      const float mb = m[j] * sl2e;
-      float p[8];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[kb * 4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r], sl2e, -mb));
-          pb[j][kb * 4 + r] = (_Float16)p[kb * 4 + r];
+        for (int r = 0; r < 4; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r], sl2e, -mb[j]));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r + 1], sl2e, -mb[j]));
+          const f16x2 pp = f16x2{(_Float16)p0, (_Float16)p1};
+          pb[j][kb * 4 + r] = pp[0];
+          pb[j][kb * 4 + r + 1] = pp[1];
+          l[j] = __builtin_amdgcn_fdot2(pp, f16x2{(_Float16)1.f, (_Float16)1.f}, l[j], false);
         }
-      l[j] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     }
+  };
+  // In-lane max of the block in st (8 scores per query and lane).
+  auto lane_max = [&](int j) {
+    return fmaxf(fmaxf(fmaxf(st[0][j][0], st[0][j][1]), fmaxf(st[0][j][2], st[0][j][3])),
+                 fmaxf(fmaxf(st[1][j][0], st[1][j][1]), fmaxf(st[1][j][2], st[1][j][3])));
   };
 
   // O^T[d][query] += V^T P^T.
@@ -320,51 +254,119 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   // MFMAs:
   //   group A  PV(s-1), QK(s), softmax(s)
   //   group B  softmax(s-1), PV(s-1), QK(s)
-  // LDS holds K(s) and V(s-1) during step s.  Block s = (K(s+1), V(s)) is
-  // loaded into registers at the start of step s and written into the other
-  // LDS stages at its end, followed by the step's only barrier.  (Measured
-  // on MI355X: this beat a barrier between the halves, per-group LDS writes
-  // inside the softmax half, loads by one group only, and a one-step-deeper
-  // register prefetch.)
+  // LDS holds K(s) and V(s-1) during step s; K(s+1) and V(s) are written
+  // into the other LDS stages at its end, followed by the step's only
+  // barrier.  They come from registers loaded one step earlier: two register
+  // buffers alternate, so a block's global loads have a whole step to
+  // arrive (with loads issued in the step that writes them, the waits for
+  // them at the step's end cost about a tenth of the kernel's time on
+  // MI355X).  Measured on MI355X as well: this beat a barrier between the
+  // halves, per-group LDS writes inside the softmax half, and loads by one
+  // group only.
+  // (grp_a is uniform across a wave.  Telling the compiler so with
+  // readfirstlane turns the two orders into scalar branches but makes the
+  // register allocation spill.)
   const bool grp_a = wave < NW / 2;
-  rows_at(krow, 0, 0);
-  rows_at(vrow, 0, 0);
-  fetch(rk, kg, krow, fk_ti, fk_u);         // K(0), all threads
-  stash_k(rk, 0);
-  auto fetch_block = [&](int b) {
-    if (b + 1 < nsteps) fetch(rk, kg, krow, fk_ti, fk_u);
-    fetch(rv, vg, vrow, fv_ti, fv_u);
-  };
-  fetch_block(0);
-  __syncthreads();
-  // Retire every outstanding load (the Q fragments included) before the
-  // loop, so that inside it the only vector-memory waits are the ones for
-  // the prefetched K/V blocks at their LDS writes.
-  __builtin_amdgcn_s_waitcnt(0);
-
-  for (int s = 0; s < nsteps; ++s) {
-    const bool more = s + 1 < nsteps;
-    if (s > 0) fetch_block(s);
-    // (Two consecutive branches, not one: this form compiles to fewer VGPRs
-    // and measured 3-4 % faster than the merged one.)
-    if (grp_a) {
-      if (s > 0) pvmm((s - 1) & 1);
-      qk(s & 1);
-    } else if (s > 0) {
-      softmax();
+  // Start of a walk over the key blocks: K(0) in LDS stage 0.  For the main
+  // walk, V stage 1 is zeroed: step 0's P.V of the nonexistent block -1
+  // reads it (with zero probabilities).
+  auto begin_walk = [&](bool main_walk) {
+    fk_ti = fk_u = fv_ti = fv_u = 0;
+    rows_at(krow, 0, 0);
+    rows_at(vrow, 0, 0);
+    fetch(rk, kg, krow, fk_ti, fk_u);
+    stash_k(rk, 0);
+    if (main_walk) {
+      uint4 *v1 = reinterpret_cast<uint4 *>(smem + 2 * KST_BYTES + VST_BYTES);
+      for (int i = tid; i < VST_BYTES / 16; i += NT) v1[i] = uint4{0u, 0u, 0u, 0u};
     }
-    if (grp_a) {
-      softmax();
-    } else {
-      if (s > 0) pvmm((s - 1) & 1);
-      qk(s & 1);
-    }
-    if (more) stash_k(rk, (s + 1) & 1);
-    stash_v(rv, s & 1);
     __syncthreads();
+    // Retire every outstanding load (the Q fragments included) before the
+    // loop, so that inside it the only vector-memory waits are the ones for
+    // the prefetched K/V blocks at their LDS writes.
+    __builtin_amdgcn_s_waitcnt(0);
+  };
+
+  if (tid == 0) flag_l[0] = 0;
+  for (int attempt = 0;; ++attempt) {
+    begin_walk(true);
+    if (attempt == 0) {
+      // Reference max: each row's max over the first key block.
+      qk(0);
+#pragma unroll
+      for (int j = 0; j < QB; ++j) m[j] = swap_max(lane_max(j));
+    }
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      mb[j] = m[j] * sl2e;
+      l[j] = 0.f;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // Group B's softmax of block -1 at step 0 must give zero
+      // probabilities, and group A's P.V of block -1 must add nothing.
+      pb[j] = f16x8{};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) st[kb][j] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+
+    // The loop has no other branches than the group's order (and the odd
+    // step count's end): fetches past the last block re-read the last key
+    // tile and are written to a stage nobody reads again.
+    Raw8<F32IN> rk2[CPT], rv2[CPT];
+    fetch(rk, kg, krow, fk_ti, fk_u);   // K(1)
+    fetch(rv, vg, vrow, fv_ti, fv_u);   // V(0)
+    auto step = [&](int s, Raw8<F32IN>(&ck)[CPT], Raw8<F32IN>(&cv)[CPT], Raw8<F32IN>(&nk)[CPT],
+                    Raw8<F32IN>(&nv)[CPT]) {
+      fetch(nk, kg, krow, fk_ti, fk_u);   // K(s+2)
+      fetch(nv, vg, vrow, fv_ti, fv_u);   // V(s+1)
+      if (grp_a) {
+        pvmm((s - 1) & 1);
+        qk(s & 1);
+      } else {
+        softmax();
+      }
+      if (grp_a) {
+        softmax();
+      } else {
+        pvmm((s - 1) & 1);
+        qk(s & 1);
+      }
+      stash_k(ck, (s + 1) & 1);
+      stash_v(cv, s & 1);
+      __syncthreads();
+    };
+    for (int s = 0; s < nsteps; s += 2) {
+      step(s, rk, rv, rk2, rv2);
+      if (s + 1 < nsteps) step(s + 1, rk2, rv2, rk, rv);
+    }
+    if (!grp_a) softmax();
+    pvmm((nsteps - 1) & 1);
+    if (attempt > 0) break;
+
+    // Did a probability of the group overflow fp16?
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) bad |= !(__builtin_fabsf(l[j]) <= 3.0e38f);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) flag_l[0] = 1;
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(flag_l[0]) == 0) break;
+
+    // Exact row maxima: S^T of every block, K through the two K stages.
+    float mx[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) mx[j] = -INFINITY;
+    begin_walk(false);
+    for (int s = 0; s < nsteps; ++s) {
+      fetch(rk, kg, krow, fk_ti, fk_u);   // K(s+1)
+      qk(s & 1);
+#pragma unroll
+      for (int j = 0; j < QB; ++j) mx[j] = fmaxf(mx[j], lane_max(j));
+      stash_k(rk, (s + 1) & 1);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < QB; ++j) m[j] = swap_max(mx[j]);
   }
-  if (!grp_a) softmax();
-  pvmm((nsteps - 1) & 1);
 
   // ---- finalize: O = O^T / l, stored row-major ----------------------------
   char *og = reinterpret_cast<char *>(a.o) + (size_t)bh * a.N * D * (F32OUT ? 4 : 2);
@@ -391,8 +393,8 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
 template <int D, int QB, int NW, bool FI, bool FO>
 hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
   auto kern = sta_fwd_kernel<D, QB, NW, FI, FO>;
-  const size_t lds = (size_t)fwd_stage_bytes(D) + sizeof(int) * ((size_t)a.V + a.max_nkv);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  const size_t lds = (size_t)fwd_lds_bytes(D, a.V, a.max_nkv);
+  if (lds > kMaxLds) return hipErrorInvalidValue;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -413,7 +415,7 @@ hipError_t launch_io(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s)
 hipError_t launch_forward(const FwdArgs &a, int variant, int head_dim, bool f32_in, bool f32_out,
                           hipStream_t stream) {
   if (a.n_blocks <= 0) return hipSuccess;
-  if (variant == 1) {
+  if (variant == kTile384) {
     if (head_dim == 128) return launch_io<128, 3, 8>(a, f32_in, f32_out, stream);
     return launch_io<64, 3, 8>(a, f32_in, f32_out, stream);
   }

@@ -132,8 +132,7 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
       p->max_nkv = std::max(p->max_nkv, p->kv_off[i + 1] - p->kv_off[i]);
     // The forward kernel keeps two K and two V stages of 32 keys plus the
     // tile-local row offsets and the item's key-tile rows in LDS (160 KiB).
-    const int64_t lds = fwd_stage_bytes(head_dim) + 4LL * (p->V + p->max_nkv);
-    if (lds > 160 * 1024) {
+    if (fwd_lds_bytes(head_dim, p->V, p->max_nkv) > kMaxLds) {
       delete p;
       return STA_ERR_UNSUPPORTED;
     }
