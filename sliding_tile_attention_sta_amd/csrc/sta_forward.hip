@@ -95,7 +95,9 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   int *off_l = flag_l + 4;
   int *kvb_l = off_l + a.V;
 
-  const int item = a.sched[blockIdx.x];
+  // The work item is uniform: readfirstlane keeps it and everything derived
+  // from it in SGPRs.
+  const int item = __builtin_amdgcn_readfirstlane(a.sched[blockIdx.x]);
   if (item < 0) return;
   const int sub = item % a.subs;
   const int rest = item / a.subs;

@@ -229,3 +229,66 @@ def test_cached_entry_point_matches_plan_entry_point():
     b2 = api.sta_forward(q, k, v, w.tile, w.windows, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, b2)
+
+
+# ---------------------------------------------------------------------------
+# The kernel's softmax keeps one reference max per query row: the row's max
+# over the first key block it visits.  A later block may exceed it by up to
+# 16 in log2 units before a probability overflows fp16; beyond that the work
+# group redoes the item against the exact row max.  This input makes that
+# happen for almost every row and checks the result against the oracle.
+# ---------------------------------------------------------------------------
+
+def test_reference_max_overflow_redo():
+    w = WORKLOADS["small"].with_heads(2)
+    say("case redo: 12x24x24 tile 6x8x8 full window, 2 heads, 1% of keys scaled x40")
+    g = torch.Generator().manual_seed(77)
+    shape = (1, w.heads, *w.video, w.head_dim)
+    q = torch.randn(shape, generator=g)
+    k = torch.randn(shape, generator=g)
+    v = torch.randn(shape, generator=g)
+    hot = torch.rand((1, 1, *w.video, 1), generator=g) < 0.01
+    k = torch.where(hot, k * 40.0, k)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+
+    plan = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    grid = O.tile_grid(w.video, w.tile)
+    tiles = [(a, b, c) for a in range(grid[0]) for b in range(grid[1]) for c in range(grid[2])]
+
+    # How far each row's max rises above its first visited block's max
+    # (keys 0..31, tile-local raster order, of the first key tile in the
+    # plan's launch order), in the kernel's exp2 units.
+    qf, kf = q.float().numpy()[0], k.float().numpy()[0]
+    l2e = 1.0 / np.log(2.0)
+    over = 0
+    rows = 0
+    for h in range(w.heads):
+        for c in tiles:
+            qt = (c[0] * grid[1] + c[1]) * grid[2] + c[2]
+            first = plan.kv_tiles(h, qt)[0]
+            fc = (first // (grid[1] * grid[2]), (first // grid[2]) % grid[1], first % grid[2])
+            qs = qf[h][tile_slice(w, c)].reshape(-1, w.head_dim).astype(np.float64)
+            ks_first = kf[h][tile_slice(w, fc)].reshape(-1, w.head_dim)[:32].astype(np.float64)
+            win = O.window_tiles(c, w.windows[h], grid)
+            ks_all = kf[h][tuple(slice(s * t, e * t) for (s, e), t in zip(win, w.tile))]
+            ks_all = ks_all.reshape(-1, w.head_dim).astype(np.float64)
+            m_first = (qs @ ks_first.T).max(axis=1) * w.scale
+            m_all = (qs @ ks_all.T).max(axis=1) * w.scale
+            over += int(((m_all - m_first) * l2e > 16.0).sum())
+            rows += qs.shape[0]
+    say(f"redo: {over} of {rows} rows exceed their first block max by more than 2^16")
+    assert over > rows // 10, "the input does not exercise the redo path"
+
+    out = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    api.sta_forward_plan(plan, q.cuda(), k.cuda(), v.cuda(), out=out, scale=w.scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    worst = (0.0, 0.0)
+    for h in range(w.heads):
+        refs = _oracle_tiles(w, q, k, v, h, tiles)
+        for c, ref in zip(tiles, refs):
+            mx, mn = errors(got[0, h][tile_slice(w, c)], ref)
+            worst = (max(worst[0], mx), max(worst[1], mn))
+            assert mx <= MAX_ABS and mn <= MEAN_ABS, (h, c, mx, mn)
+    say(f"redo worst max {worst[0]:.2e} worst tile mean {worst[1]:.2e}")
