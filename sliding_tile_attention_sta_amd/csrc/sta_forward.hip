@@ -17,17 +17,15 @@
 //     accumulator layout a lane holds one query and 4 keys of each 16x16
 //     block.
 //   * Softmax in fp32 with exp2 and the scale folded into one FMA, against
-//     one reference max per query row for the whole walk: the accumulators
-//     are never rescaled and a step computes no row max, which takes about a
-//     fifth of the VALU work off the step (the kernel is bound by VALU issue,
-//     not by the MFMAs).  The first attempt takes each row's max over the
-//     first key block.  Later blocks may exceed it; probabilities are rounded
-//     to fp16 (nearest even), which holds values up to 65504, and one that
-//     overflows becomes +inf, and so does its row sum.  A work group that
-//     finds a non-finite row sum at the end computes the exact row maxima with
-//     a pass of S^T only (bitwise the same scores) and walks again, now with
-//     every probability <= 1.  For ordinary inputs the first block's max lies
-//     within a few units of the row max and the second walk never runs.
+//     one reference max per query row that starts as the row's max over the
+//     first key block and moves only when it must: probabilities are rounded
+//     to fp16 (nearest even), which holds values up to 65504, so a block
+//     whose scores exceed the reference by less than 16 (exp2 units) needs
+//     nothing, and a larger excess overflows to +inf in the row sum, which a
+//     compare per step detects and a rare repair fixes (new reference = row
+//     max, O and l rescaled, the block's probabilities recomputed).  A step
+//     therefore computes no row max, which takes about a third of the VALU
+//     work off it (the kernel is bound by VALU issue more than by the MFMAs).
 //   * fp16 keeps 11 significant bits against bf16's 8, which cuts the error
 //     of the weighted sum about tenfold when a few keys dominate a row.  The
 //     row sum is accumulated from the rounded probabilities with
@@ -88,11 +86,9 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   constexpr int DC = D / 32;                      // 32-wide d chunks (QK^T K-dim steps)
   constexpr int DB = D / 16;                      // 16-wide d blocks (rows of O^T)
 
-  // LDS: K stages, V stages, a flag word (16 bytes), tile-local row
-  // offsets, key-tile base rows.
+  // LDS: K stages, V stages, tile-local row offsets, key-tile base rows.
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  int *flag_l = reinterpret_cast<int *>(smem + 2 * KST_BYTES + 2 * VST_BYTES);
-  int *off_l = flag_l + 4;
+  int *off_l = reinterpret_cast<int *>(smem + 2 * KST_BYTES + 2 * VST_BYTES);
   int *kvb_l = off_l + a.V;
 
   // The work item is uniform: readfirstlane keeps it and everything derived
@@ -207,29 +203,58 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // Softmax against the fixed reference: lane holds query 16j + l16, keys
-  // 4g + r and 16 + 4g + r.  l is the lane's partial row sum.
-  float mb[QB];      // reference max * scale * log2(e)
-  auto softmax = [&]() {
-#pragma unroll
-    for (int j = 0; j < QB; ++j) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r], sl2e, -mb[j]));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r + 1], sl2e, -mb[j]));
-          const f16x2 pp = f16x2{(_Float16)p0, (_Float16)p1};
-          pb[j][kb * 4 + r] = pp[0];
-          pb[j][kb * 4 + r + 1] = pp[1];
-          l[j] = __builtin_amdgcn_fdot2(pp, f16x2{(_Float16)1.f, (_Float16)1.f}, l[j], false);
-        }
-    }
-  };
   // In-lane max of the block in st (8 scores per query and lane).
   auto lane_max = [&](int j) {
     return fmaxf(fmaxf(fmaxf(st[0][j][0], st[0][j][1]), fmaxf(st[0][j][2], st[0][j][3])),
                  fmaxf(fmaxf(st[1][j][0], st[1][j][1]), fmaxf(st[1][j][2], st[1][j][3])));
+  };
+  // Probabilities of the block in st against each row's reference max m:
+  // lane holds query 16j + l16, keys 4g + r and 16 + 4g + r.  They go to pb
+  // in fp16; their sum over the lane's keys is added to acc.
+  float mb[QB];      // m * scale * log2(e)
+  auto probs = [&](int j, float &acc) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r], sl2e, -mb[j]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r + 1], sl2e, -mb[j]));
+        const f16x2 pp = f16x2{(_Float16)p0, (_Float16)p1};
+        pb[j][kb * 4 + r] = pp[0];
+        pb[j][kb * 4 + r + 1] = pp[1];
+        acc = __builtin_amdgcn_fdot2(pp, f16x2{(_Float16)1.f, (_Float16)1.f}, acc, false);
+      }
+  };
+  // Softmax of one block.  The new row sums are checked before they replace
+  // l: an overflowed probability makes its row sum +inf, and then the wave
+  // repairs the block (reference moved to the row max, O and l rescaled,
+  // probabilities recomputed, now <= 1).  O is in VGPRs, so the rescale
+  // needs no register copies.
+  auto softmax = [&]() {
+    float ln[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      ln[j] = l[j];
+      probs(j, ln[j]);
+    }
+    float lmax = ln[0];
+#pragma unroll
+    for (int j = 1; j < QB; ++j) lmax = fmaxf(lmax, ln[j]);
+    if (__builtin_amdgcn_ballot_w64(!(lmax <= 3.0e38f))) {
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const float mnew = fmaxf(m[j], swap_max(lane_max(j)));
+        const float alpha = __builtin_amdgcn_exp2f((m[j] - mnew) * sl2e);
+        m[j] = mnew;
+        mb[j] = mnew * sl2e;
+        ln[j] = l[j] * alpha;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) o[b][j] *= alpha;
+        probs(j, ln[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < QB; ++j) l[j] = ln[j];
   };
 
   // O^T[d][query] += V^T P^T.
@@ -269,19 +294,16 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   // readfirstlane turns the two orders into scalar branches but makes the
   // register allocation spill.)
   const bool grp_a = wave < NW / 2;
-  // Start of a walk over the key blocks: K(0) in LDS stage 0.  For the main
-  // walk, V stage 1 is zeroed: step 0's P.V of the nonexistent block -1
-  // reads it (with zero probabilities).
-  auto begin_walk = [&](bool main_walk) {
-    fk_ti = fk_u = fv_ti = fv_u = 0;
+  // Start of the walk over the key blocks: K(0) in LDS stage 0, V stage 1
+  // zeroed (step 0's P.V of the nonexistent block -1 reads it, with zero
+  // probabilities).
+  auto begin_walk = [&]() {
     rows_at(krow, 0, 0);
     rows_at(vrow, 0, 0);
     fetch(rk, kg, krow, fk_ti, fk_u);
     stash_k(rk, 0);
-    if (main_walk) {
-      uint4 *v1 = reinterpret_cast<uint4 *>(smem + 2 * KST_BYTES + VST_BYTES);
-      for (int i = tid; i < VST_BYTES / 16; i += NT) v1[i] = uint4{0u, 0u, 0u, 0u};
-    }
+    uint4 *v1 = reinterpret_cast<uint4 *>(smem + 2 * KST_BYTES + VST_BYTES);
+    for (int i = tid; i < VST_BYTES / 16; i += NT) v1[i] = uint4{0u, 0u, 0u, 0u};
     __syncthreads();
     // Retire every outstanding load (the Q fragments included) before the
     // loop, so that inside it the only vector-memory waits are the ones for
@@ -289,86 +311,55 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
   };
 
-  if (tid == 0) flag_l[0] = 0;
-  for (int attempt = 0;; ++attempt) {
-    begin_walk(true);
-    if (attempt == 0) {
-      // Reference max: each row's max over the first key block.
-      qk(0);
+  begin_walk();
+  // Initial reference max: each row's max over the first key block.
+  qk(0);
 #pragma unroll
-      for (int j = 0; j < QB; ++j) m[j] = swap_max(lane_max(j));
-    }
+  for (int j = 0; j < QB; ++j) {
+    m[j] = swap_max(lane_max(j));
+    mb[j] = m[j] * sl2e;
+    l[j] = 0.f;
 #pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      mb[j] = m[j] * sl2e;
-      l[j] = 0.f;
+    for (int b = 0; b < DB; ++b) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Group B's softmax of block -1 at step 0 must give zero probabilities,
+    // and group A's P.V of block -1 must add nothing.
+    pb[j] = f16x8{};
 #pragma unroll
-      for (int b = 0; b < DB; ++b) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // Group B's softmax of block -1 at step 0 must give zero
-      // probabilities, and group A's P.V of block -1 must add nothing.
-      pb[j] = f16x8{};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) st[kb][j] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    }
-
-    // The loop has no other branches than the group's order (and the odd
-    // step count's end): fetches past the last block re-read the last key
-    // tile and are written to a stage nobody reads again.
-    Raw8<F32IN> rk2[CPT], rv2[CPT];
-    fetch(rk, kg, krow, fk_ti, fk_u);   // K(1)
-    fetch(rv, vg, vrow, fv_ti, fv_u);   // V(0)
-    auto step = [&](int s, Raw8<F32IN>(&ck)[CPT], Raw8<F32IN>(&cv)[CPT], Raw8<F32IN>(&nk)[CPT],
-                    Raw8<F32IN>(&nv)[CPT]) {
-      fetch(nk, kg, krow, fk_ti, fk_u);   // K(s+2)
-      fetch(nv, vg, vrow, fv_ti, fv_u);   // V(s+1)
-      if (grp_a) {
-        pvmm((s - 1) & 1);
-        qk(s & 1);
-      } else {
-        softmax();
-      }
-      if (grp_a) {
-        softmax();
-      } else {
-        pvmm((s - 1) & 1);
-        qk(s & 1);
-      }
-      stash_k(ck, (s + 1) & 1);
-      stash_v(cv, s & 1);
-      __syncthreads();
-    };
-    for (int s = 0; s < nsteps; s += 2) {
-      step(s, rk, rv, rk2, rv2);
-      if (s + 1 < nsteps) step(s + 1, rk2, rv2, rk, rv);
-    }
-    if (!grp_a) softmax();
-    pvmm((nsteps - 1) & 1);
-    if (attempt > 0) break;
-
-    // Did a probability of the group overflow fp16?
-    bool bad = false;
-#pragma unroll
-    for (int j = 0; j < QB; ++j) bad |= !(__builtin_fabsf(l[j]) <= 3.0e38f);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) flag_l[0] = 1;
-    __syncthreads();
-    if (__builtin_amdgcn_readfirstlane(flag_l[0]) == 0) break;
-
-    // Exact row maxima: S^T of every block, K through the two K stages.
-    float mx[QB];
-#pragma unroll
-    for (int j = 0; j < QB; ++j) mx[j] = -INFINITY;
-    begin_walk(false);
-    for (int s = 0; s < nsteps; ++s) {
-      fetch(rk, kg, krow, fk_ti, fk_u);   // K(s+1)
-      qk(s & 1);
-#pragma unroll
-      for (int j = 0; j < QB; ++j) mx[j] = fmaxf(mx[j], lane_max(j));
-      stash_k(rk, (s + 1) & 1);
-      __syncthreads();
-    }
-#pragma unroll
-    for (int j = 0; j < QB; ++j) m[j] = swap_max(mx[j]);
+    for (int kb = 0; kb < 2; ++kb) st[kb][j] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   }
+
+  // The loop has no other branches than the group's order (and the odd
+  // step count's end): fetches past the last block re-read the last key
+  // tile and are written to a stage nobody reads again.
+  Raw8<F32IN> rk2[CPT], rv2[CPT];
+  fetch(rk, kg, krow, fk_ti, fk_u);   // K(1)
+  fetch(rv, vg, vrow, fv_ti, fv_u);   // V(0)
+  auto step = [&](int s, Raw8<F32IN>(&ck)[CPT], Raw8<F32IN>(&cv)[CPT], Raw8<F32IN>(&nk)[CPT],
+                  Raw8<F32IN>(&nv)[CPT]) {
+    fetch(nk, kg, krow, fk_ti, fk_u);   // K(s+2)
+    fetch(nv, vg, vrow, fv_ti, fv_u);   // V(s+1)
+    if (grp_a) {
+      pvmm((s - 1) & 1);
+      qk(s & 1);
+    } else {
+      softmax();
+    }
+    if (grp_a) {
+      softmax();
+    } else {
+      pvmm((s - 1) & 1);
+      qk(s & 1);
+    }
+    stash_k(ck, (s + 1) & 1);
+    stash_v(cv, s & 1);
+    __syncthreads();
+  };
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, rk, rv, rk2, rv2);
+    if (s + 1 < nsteps) step(s + 1, rk2, rv2, rk, rv);
+  }
+  if (!grp_a) softmax();
+  pvmm((nsteps - 1) & 1);
 
   // ---- finalize: O = O^T / l, stored row-major ----------------------------
   char *og = reinterpret_cast<char *>(a.o) + (size_t)bh * a.N * D * (F32OUT ? 4 : 2);

@@ -30,10 +30,10 @@ constexpr int kMaxTileTokens = 4096;
 constexpr int fwd_kstride(int head_dim) { return 2 * head_dim + 32; }
 constexpr int fwd_vstride(int head_dim) { return 2 * head_dim + 32; }
 // Dynamic LDS of a forward launch: two K and two V stages of kKeyBlock keys,
-// a 16-byte flag word, the tile-local row offsets (tile_tokens ints) and the
-// key-tile base rows of the item (max_nkv ints).
+// the tile-local row offsets (tile_tokens ints) and the key-tile base rows of
+// the item (max_nkv ints).
 constexpr long long fwd_lds_bytes(int head_dim, long long tile_tokens, long long max_nkv) {
-  return 2LL * kKeyBlock * (fwd_kstride(head_dim) + fwd_vstride(head_dim)) + 16 +
+  return 2LL * kKeyBlock * (fwd_kstride(head_dim) + fwd_vstride(head_dim)) +
          4LL * (tile_tokens + max_nkv);
 }
 constexpr long long kMaxLds = 160 * 1024;

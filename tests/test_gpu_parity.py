@@ -232,16 +232,16 @@ def test_cached_entry_point_matches_plan_entry_point():
 
 
 # ---------------------------------------------------------------------------
-# The kernel's softmax keeps one reference max per query row: the row's max
-# over the first key block it visits.  A later block may exceed it by up to
-# 16 in log2 units before a probability overflows fp16; beyond that the work
-# group redoes the item against the exact row max.  This input makes that
-# happen for almost every row and checks the result against the oracle.
+# The kernel's softmax keeps one reference max per query row, which starts
+# as the row's max over the first key block it visits and moves only when a
+# block's probabilities overflow fp16 (scores more than 16 above it in log2
+# units): the kernel then repairs that block.  This input makes that happen
+# for almost every row and checks the result against the oracle.
 # ---------------------------------------------------------------------------
 
-def test_reference_max_overflow_redo():
+def test_reference_max_overflow_repair():
     w = WORKLOADS["small"].with_heads(2)
-    say("case redo: 12x24x24 tile 6x8x8 full window, 2 heads, 1% of keys scaled x40")
+    say("case repair: 12x24x24 tile 6x8x8 full window, 2 heads, 1% of keys scaled x40")
     g = torch.Generator().manual_seed(77)
     shape = (1, w.heads, *w.video, w.head_dim)
     q = torch.randn(shape, generator=g)
@@ -276,8 +276,8 @@ def test_reference_max_overflow_redo():
             m_all = (qs @ ks_all.T).max(axis=1) * w.scale
             over += int(((m_all - m_first) * l2e > 16.0).sum())
             rows += qs.shape[0]
-    say(f"redo: {over} of {rows} rows exceed their first block max by more than 2^16")
-    assert over > rows // 10, "the input does not exercise the redo path"
+    say(f"repair: {over} of {rows} rows exceed their first block max by more than 2^16")
+    assert over > rows // 10, "the input does not exercise the repair path"
 
     out = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
     api.sta_forward_plan(plan, q.cuda(), k.cuda(), v.cuda(), out=out, scale=w.scale)
@@ -291,4 +291,4 @@ def test_reference_max_overflow_redo():
             mx, mn = errors(got[0, h][tile_slice(w, c)], ref)
             worst = (max(worst[0], mx), max(worst[1], mn))
             assert mx <= MAX_ABS and mn <= MEAN_ABS, (h, c, mx, mn)
-    say(f"redo worst max {worst[0]:.2e} worst tile mean {worst[1]:.2e}")
+    say(f"repair worst max {worst[0]:.2e} worst tile mean {worst[1]:.2e}")
