@@ -15,7 +15,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "sample_query_tiles", "tile_count"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_grad_out", "sample_query_tiles", "tile_count"]
 
 
 @dataclass(frozen=True)
@@ -106,6 +106,21 @@ def make_qkv(w: Workload, device: str | torch.device = "cpu"):
             m.uniform_(lo, hi, generator=g)
             out[i].mul_(m)
     return tuple(x.to(w.torch_dtype) for x in out)
+
+
+def make_grad_out(w: Workload, device: str | torch.device = "cpu"):
+    """The upstream gradient dL/dO for backward runs, natural layout
+    [B, heads, T, H, W, D]: N(0, 1) from a generator seeded with
+    1000 * index + 500 on ``device``, cast to the workload's dtype.  The
+    pages fine-tune on real videos; a unit normal stands in for that
+    gradient."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 500)
+    T, H, W = w.video
+    x = torch.randn((w.batch, w.heads, T, H, W, w.head_dim), generator=g, device=dev,
+                    dtype=torch.float32)
+    return x.to(w.torch_dtype)
 
 
 def sample_query_tiles(w: Workload, head: int, count: int = 64) -> list[tuple[int, int, int]]:
