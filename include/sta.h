@@ -1,5 +1,5 @@
 /*
- * sta.h -- C ABI of the MI355X (gfx950) Sliding Tile Attention forward library.
+ * sta.h -- C ABI of the MI355X (gfx950) Sliding Tile Attention library (forward and backward).
  *
  * Operation (source: "Fast Video Generation with Sliding Tile Attention",
  * arXiv 2502.04507 -- index page, section "Abstract"; gptget summary page,
@@ -72,6 +72,10 @@ typedef struct {
   int64_t work_items;       /* launched work items (including idle padding items) */
   int32_t queries_per_item; /* query tokens per work item */
   int32_t kernel_variant;   /* 0 = generic (32 queries / item), 1 = 384-query items */
+  int32_t bwd_supported;    /* 1 if sta_backward_plan accepts this plan */
+  int32_t bwd_tokens_per_item; /* queries (dQ) or keys (dK/dV) per backward work item */
+  int64_t bwd_items_dq;     /* launched dQ work items (including idle padding) */
+  int64_t bwd_items_dkdv;   /* launched dK/dV work items (including idle padding) */
 } sta_plan_info;
 
 /* Build the host plan: tile grid, clamped per-head windows, per-(head, query
@@ -104,11 +108,24 @@ sta_status sta_plan_perm(const sta_plan *plan, int32_t *perm, int64_t cap);
 sta_status sta_plan_kv_tiles(const sta_plan *plan, int head, int q_tile, int32_t *out, int cap,
                              int *count);
 
+/* Query tiles (raster indices, ascending) whose window holds key tile
+ * kv_tile for head head: the inverse of sta_plan_kv_tiles, walked by the
+ * backward's dK/dV kernel.  Buffer and error conventions as sta_plan_kv_tiles. */
+sta_status sta_plan_q_tiles(const sta_plan *plan, int head, int kv_tile, int32_t *out, int cap,
+                            int *count);
+
 /* The launch schedule: item codes in launch order, -1 for idle padding items.
  * A code encodes ((b * heads + h) * n_tiles + q_tile) * subs + sub, where
  * subs = tile_tokens / queries_per_item.  out: host buffer of cap int32;
  * *count receives the item count (STA_ERR_ARG if it exceeds cap). */
 sta_status sta_plan_schedule(const sta_plan *plan, int32_t *out, int64_t cap, int64_t *count);
+
+/* The backward schedules, same conventions: which = 0 for the dQ kernel
+ * (code ((b * heads + h) * n_tiles + q_tile) * subs + sub), 1 for the dK/dV
+ * kernel (the same with the key tile), subs = tile_tokens /
+ * bwd_tokens_per_item.  Empty when bwd_supported is 0. */
+sta_status sta_plan_schedule_bwd(const sta_plan *plan, int which, int32_t *out, int64_t cap,
+                                 int64_t *count);
 
 /* Gather a [batch, heads, N, head_dim] tensor from natural into tile-major
  * token order (out[.., p, :] = in[.., perm[p], :]), or back.  dtype is the
@@ -132,6 +149,49 @@ sta_status sta_tile_unreorder(const sta_plan *plan, const void *in, void *out, s
 sta_status sta_forward_plan(const sta_plan *plan, const void *q, const void *k, const void *v,
                             void *out, float scale, sta_dtype in_dtype, sta_dtype out_dtype,
                             sta_layout layout, void *stream);
+
+/* STA forward that also writes the row log-sum-exp the backward needs.
+ *   lse: caller-owned device buffer of batch*heads*N float, same token order
+ *        as layout; lse[x] = ln(sum_j exp(scale * q_x.k_j)) over the keys of
+ *        x's window (natural log, scale applied), computed from the same
+ *        rounded probabilities as out.
+ * Everything else as sta_forward_plan; lse must not overlap any tensor.
+ * STA_ERR_ARG for a NULL lse. */
+sta_status sta_forward_plan_lse(const sta_plan *plan, const void *q, const void *k, const void *v,
+                                void *out, float *lse, float scale, sta_dtype in_dtype,
+                                sta_dtype out_dtype, sta_layout layout, void *stream);
+
+/* STA backward: gradients of <out, dout> with respect to q, k and v, where
+ * out is STA's output for (q, k, v).  Defined by the chain rule of the
+ * forward (the pages fine-tune through the operator; index page, Abstract,
+ * and gptget summary page, Summary): with P_xj = exp(scale q_x.k_j - lse_x)
+ * over the keys j of x's window,
+ *     dv_j = sum_x P_xj dout_x
+ *     dS_xj = P_xj (dout_x.v_j - delta_x),  delta_x = dout_x . out_x
+ *     dq_x = scale sum_j dS_xj k_j,        dk_j = scale sum_x dS_xj q_x
+ * where x runs over the queries whose window holds key j.
+ *   q, k, v, dout: [batch, heads, N, head_dim] of in_dtype.
+ *   out: the forward's output, out_dtype; lse: the forward's row log-sum-exp
+ *        (sta_forward_plan_lse with the same q, k, v, scale and plan).
+ *   delta: caller-owned device scratch of batch*heads*N float, overwritten
+ *        with delta_x.
+ *   dq, dk, dv: outputs, grad_dtype (STA_F32 or STA_BF16), same shape.
+ * All tensors use the token order given by layout.  Written buffers (delta,
+ * dq, dk, dv) must not overlap each other or any input.
+ * Precision: every product runs on fp16 MFMA with fp32 accumulation; q and k
+ * enter as the bf16 values the forward used (STA_F32 inputs rounded to bf16,
+ * nearest-even), v and dout are converted to fp16 (exact for bf16 values in
+ * range, nearest-even for fp32), and P and dS are rounded to fp16.  Entries
+ * of q, k, v and dout and the products dS must lie within the fp16 range.
+ * Deterministic: no atomics; dq and dk/dv come from separate kernels.
+ * Errors: STA_ERR_ARG (NULL, bad enum, scale <= 0, overlap),
+ * STA_ERR_UNSUPPORTED (the plan's tile volume and window lists exceed the
+ * backward kernels' LDS), STA_ERR_HIP. */
+sta_status sta_backward_plan(const sta_plan *plan, const void *q, const void *k, const void *v,
+                             const void *out, const void *dout, const float *lse, float *delta,
+                             void *dq, void *dk, void *dv, float scale, sta_dtype in_dtype,
+                             sta_dtype out_dtype, sta_dtype grad_dtype, sta_layout layout,
+                             void *stream);
 
 /* Same, building (or finding in a process-wide cache keyed by every shape
  * and window argument) the plan itself.  Cached plans live until

@@ -1,4 +1,4 @@
-"""Sliding Tile Attention (STA) forward for AMD MI355X (gfx950).
+"""Sliding Tile Attention (STA) forward and backward for AMD MI355X (gfx950).
 
 The compute path is the C-ABI library ``libsta.so`` (declared in
 ``include/sta.h``); this package only marshals torch tensors into it.
@@ -7,6 +7,8 @@ The compute path is the C-ABI library ``libsta.so`` (declared in
 from .api import (  # noqa: F401
     Plan,
     StaError,
+    sta_attention,
+    sta_backward_plan,
     sta_clear_plan_cache,
     sta_forward,
     sta_forward_plan,

@@ -24,7 +24,9 @@ class PlanInfo(ctypes.Structure):
         ("tile_tokens", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
         ("tokens", ctypes.c_int64), ("pairs", ctypes.c_int64), ("flops", ctypes.c_double),
         ("work_items", ctypes.c_int64), ("queries_per_item", ctypes.c_int32),
-        ("kernel_variant", ctypes.c_int32),
+        ("kernel_variant", ctypes.c_int32), ("bwd_supported", ctypes.c_int32),
+        ("bwd_tokens_per_item", ctypes.c_int32), ("bwd_items_dq", ctypes.c_int64),
+        ("bwd_items_dkdv", ctypes.c_int64),
     ]
 
 
@@ -42,9 +44,14 @@ SIGNATURES = {
     "sta_plan_perm": (_I, [_P, _I32P, _I64]),
     "sta_plan_kv_tiles": (_I, [_P, _I, _I, _I32P, _I, _IP]),
     "sta_plan_schedule": (_I, [_P, _I32P, _I64, ctypes.POINTER(_I64)]),
+    "sta_plan_q_tiles": (_I, [_P, _I, _I, _I32P, _I, _IP]),
+    "sta_plan_schedule_bwd": (_I, [_P, _I, _I32P, _I64, ctypes.POINTER(_I64)]),
     "sta_tile_reorder": (_I, [_P, _P, _P, _I, _P]),
     "sta_tile_unreorder": (_I, [_P, _P, _P, _I, _P]),
     "sta_forward_plan": (_I, [_P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I, _P]),
+    "sta_forward_plan_lse": (_I, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I, _P]),
+    "sta_backward_plan": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I,
+                               _I, _P]),
     "sta_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _IP, _IP, _I, ctypes.c_float,
                          _I, _I, _I, _P]),
     "sta_clear_plan_cache": (_I, []),

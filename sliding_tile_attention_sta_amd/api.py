@@ -17,7 +17,7 @@ from . import _lib as L
 
 __all__ = [
     "Plan", "sta_plan_create", "sta_tile_reorder", "sta_tile_unreorder", "sta_forward_plan",
-    "sta_forward", "sta_clear_plan_cache", "StaError",
+    "sta_backward_plan", "sta_attention", "sta_forward", "sta_clear_plan_cache", "StaError",
 ]
 
 StaError = L.StaError
@@ -95,6 +95,23 @@ class Plan:
                 "sta_plan_kv_tiles")
         return list(buf[:cnt.value])
 
+    def q_tiles(self, head: int, kv_tile: int) -> list[int]:
+        cnt = ctypes.c_int()
+        L.lib().sta_plan_q_tiles(self._h, head, kv_tile, None, 0, ctypes.byref(cnt))
+        buf = (ctypes.c_int32 * max(1, cnt.value))()
+        L.check(L.lib().sta_plan_q_tiles(self._h, head, kv_tile, buf, cnt.value, ctypes.byref(cnt)),
+                "sta_plan_q_tiles")
+        return list(buf[:cnt.value])
+
+    def schedule_bwd(self, which: int) -> torch.Tensor:
+        """Backward launch schedule: which = 0 (dQ) or 1 (dK/dV)."""
+        n = ctypes.c_int64()
+        L.lib().sta_plan_schedule_bwd(self._h, which, None, 0, ctypes.byref(n))
+        out = torch.empty(max(1, n.value), dtype=torch.int32)
+        L.check(L.lib().sta_plan_schedule_bwd(self._h, which, ctypes.cast(out.data_ptr(), L._I32P),
+                                              n.value, ctypes.byref(n)), "sta_plan_schedule_bwd")
+        return out[:n.value]
+
     def schedule(self) -> torch.Tensor:
         n = ctypes.c_int64()
         L.lib().sta_plan_schedule(self._h, None, 0, ctypes.byref(n))
@@ -143,8 +160,22 @@ def sta_tile_unreorder(plan: Plan, x: torch.Tensor, out: torch.Tensor | None = N
     return _reorder(L.lib().sta_tile_unreorder, plan, x, out, stream)
 
 
+def _check_rows(x: torch.Tensor, plan: Plan, name: str):
+    i = plan.info
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or not x.is_contiguous() \
+            or x.dtype != torch.float32 or x.numel() != i.batch * i.heads * i.tokens:
+        raise ValueError(f"{name}: contiguous CUDA float32 tensor of batch*heads*N elements required")
+
+
+def _ptr(x):
+    return ctypes.c_void_p(x.data_ptr())
+
+
 def sta_forward_plan(plan: Plan, q, k, v, out=None, scale: float | None = None,
-                     out_dtype=torch.float32, layout: str = "natural", stream=None):
+                     out_dtype=torch.float32, layout: str = "natural", stream=None, lse=None):
+    """STA forward with a plan.  When ``lse`` is given ([B, heads, N]-sized
+    float32 tensor, or True to allocate one) the row log-sum-exp is written
+    too and ``(out, lse)`` is returned."""
     for name, x in (("q", q), ("k", k), ("v", v)):
         _check_tensor(x, plan, name)
     if not (q.dtype == k.dtype == v.dtype):
@@ -154,12 +185,75 @@ def sta_forward_plan(plan: Plan, q, k, v, out=None, scale: float | None = None,
     _check_tensor(out, plan, "out")
     if scale is None:
         scale = 1.0 / math.sqrt(plan.info.head_dim)
-    st = L.lib().sta_forward_plan(plan.handle, ctypes.c_void_p(q.data_ptr()),
-                                  ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-                                  ctypes.c_void_p(out.data_ptr()), float(scale), _DTYPES[q.dtype],
-                                  _DTYPES[out.dtype], _LAYOUTS[layout], _stream(stream))
-    L.check(st, "sta_forward_plan")
-    return out
+    args = (plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out))
+    tail = (float(scale), _DTYPES[q.dtype], _DTYPES[out.dtype], _LAYOUTS[layout], _stream(stream))
+    if lse is None or lse is False:
+        L.check(L.lib().sta_forward_plan(*args, *tail), "sta_forward_plan")
+        return out
+    if lse is True:
+        i = plan.info
+        lse = torch.empty((i.batch, i.heads, i.tokens), dtype=torch.float32, device=q.device)
+    _check_rows(lse, plan, "lse")
+    L.check(L.lib().sta_forward_plan_lse(*args, _ptr(lse), *tail), "sta_forward_plan_lse")
+    return out, lse
+
+
+def sta_backward_plan(plan: Plan, q, k, v, out, dout, lse, scale: float | None = None,
+                      grad_dtype=torch.float32, layout: str = "natural", dq=None, dk=None, dv=None,
+                      delta=None, stream=None):
+    """STA backward: (dq, dk, dv) of <out, dout>.  ``out`` and ``lse`` come
+    from ``sta_forward_plan(..., lse=True)`` on the same inputs."""
+    for name, x in (("q", q), ("k", k), ("v", v), ("dout", dout), ("out", out)):
+        _check_tensor(x, plan, name)
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype):
+        raise ValueError("q, k, v, dout must share a dtype")
+    _check_rows(lse, plan, "lse")
+    i = plan.info
+    if delta is None:
+        delta = torch.empty((i.batch, i.heads, i.tokens), dtype=torch.float32, device=q.device)
+    _check_rows(delta, plan, "delta")
+    grads = []
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if g is None:
+            g = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+        _check_tensor(g, plan, name)
+        grads.append(g)
+    if not (grads[0].dtype == grads[1].dtype == grads[2].dtype):
+        raise ValueError("dq, dk, dv must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(i.head_dim)
+    st = L.lib().sta_backward_plan(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                   _ptr(lse), _ptr(delta), *(_ptr(g) for g in grads), float(scale),
+                                   _DTYPES[q.dtype], _DTYPES[out.dtype], _DTYPES[grads[0].dtype],
+                                   _LAYOUTS[layout], _stream(stream))
+    L.check(st, "sta_backward_plan")
+    return tuple(grads)
+
+
+class _StaAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, plan, scale, layout):
+        q, k, v = (x.contiguous() for x in (q, k, v))
+        out, lse = sta_forward_plan(plan, q, k, v, scale=scale, out_dtype=q.dtype, layout=layout,
+                                    lse=True)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.plan, ctx.scale, ctx.layout = plan, scale, layout
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        dq, dk, dv = sta_backward_plan(ctx.plan, q, k, v, out, dout.contiguous().to(q.dtype), lse,
+                                       scale=ctx.scale, grad_dtype=q.dtype, layout=ctx.layout)
+        return dq, dk, dv, None, None, None
+
+
+def sta_attention(q, k, v, plan: Plan, scale: float | None = None, layout: str = "natural"):
+    """Differentiable STA (autograd through the library's forward and
+    backward).  Output and gradients have q's dtype."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(plan.info.head_dim)
+    return _StaAttention.apply(q, k, v, plan, float(scale), layout)
 
 
 def sta_forward(q, k, v, tile, windows, scale: float | None = None, out=None,

@@ -33,16 +33,18 @@ sta_status device_tables(const sta_plan *p, DeviceTables *out) {
   std::vector<int32_t> base_tm(p->n_tiles), off_tm(p->V);
   for (int i = 0; i < p->n_tiles; ++i) base_tm[i] = i * p->V;
   for (int j = 0; j < p->V; ++j) off_tm[j] = j;
-  const std::vector<int32_t> *parts[] = {&p->kv_off, &p->kv_idx, &p->sched, &p->base_nat,
-                                         &p->off_nat, &base_tm, &off_tm};
-  size_t offs[7], total = 0;
-  for (int i = 0; i < 7; ++i) {
+  const std::vector<int32_t> *parts[] = {&p->kv_off, &p->kv_idx,   &p->sched,    &p->base_nat,
+                                         &p->off_nat, &base_tm,     &off_tm,      &p->q_off,
+                                         &p->q_idx,   &p->sched_dq, &p->sched_dkdv};
+  constexpr int kParts = sizeof(parts) / sizeof(parts[0]);
+  size_t offs[kParts], total = 0;
+  for (int i = 0; i < kParts; ++i) {
     offs[i] = total;
     total += (parts[i]->size() * sizeof(int32_t) + 255) & ~size_t(255);
   }
   void *block = nullptr;
   if (hipMalloc(&block, total) != hipSuccess) return STA_ERR_ALLOC;
-  for (int i = 0; i < 7; ++i) {
+  for (int i = 0; i < kParts; ++i) {
     if (parts[i]->empty()) continue;
     if (hipMemcpy(static_cast<char *>(block) + offs[i], parts[i]->data(),
                   parts[i]->size() * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess) {
@@ -59,6 +61,10 @@ sta_status device_tables(const sta_plan *p, DeviceTables *out) {
   t.off_nat = reinterpret_cast<int32_t *>(b + offs[4]);
   t.base_tm = reinterpret_cast<int32_t *>(b + offs[5]);
   t.off_tm = reinterpret_cast<int32_t *>(b + offs[6]);
+  t.q_off = reinterpret_cast<int32_t *>(b + offs[7]);
+  t.q_idx = reinterpret_cast<int32_t *>(b + offs[8]);
+  t.sched_dq = reinterpret_cast<int32_t *>(b + offs[9]);
+  t.sched_dkdv = reinterpret_cast<int32_t *>(b + offs[10]);
   t.block = block;
   p->dev[dev] = t;
   *out = t;
@@ -124,9 +130,13 @@ sta_status sta_tile_unreorder(const sta_plan *plan, const void *in, void *out, s
   return sta::reorder(plan, in, out, dtype, stream, 1);
 }
 
-sta_status sta_forward_plan(const sta_plan *p, const void *q, const void *k, const void *v,
-                            void *out, float scale, sta_dtype in_dtype, sta_dtype out_dtype,
-                            sta_layout layout, void *stream) {
+}  // extern "C"
+
+namespace sta {
+namespace {
+
+sta_status forward(const sta_plan *p, const void *q, const void *k, const void *v, void *out, float *lse,
+                   float scale, sta_dtype in_dtype, sta_dtype out_dtype, sta_layout layout, void *stream) {
   if (!p || !q || !k || !v || !out) return STA_ERR_ARG;
   if (!sta::valid_dtype(in_dtype) || !sta::valid_dtype(out_dtype)) return STA_ERR_ARG;
   if (layout != STA_LAYOUT_NATURAL && layout != STA_LAYOUT_TILE_MAJOR) return STA_ERR_ARG;
@@ -135,6 +145,12 @@ sta_status sta_forward_plan(const sta_plan *p, const void *q, const void *k, con
   const size_t ib = elems * sta::dtype_bytes(in_dtype), ob = elems * sta::dtype_bytes(out_dtype);
   if (sta::overlaps(out, ob, q, ib) || sta::overlaps(out, ob, k, ib) || sta::overlaps(out, ob, v, ib))
     return STA_ERR_ARG;
+  if (lse) {
+    const size_t lb = (size_t)p->batch * p->heads * p->N * sizeof(float);
+    if (overlaps(lse, lb, q, ib) || overlaps(lse, lb, k, ib) || overlaps(lse, lb, v, ib) ||
+        overlaps(lse, lb, out, ob))
+      return STA_ERR_ARG;
+  }
   sta::DeviceTables t;
   sta_status st = sta::device_tables(p, &t);
   if (st != STA_OK) return st;
@@ -153,9 +169,98 @@ sta_status sta_forward_plan(const sta_plan *p, const void *q, const void *k, con
   a.sl2e = scale * 1.44269504088896340736f;
   a.n_blocks = (int32_t)p->sched.size();
   a.max_nkv = p->max_nkv;
+  a.lse = lse;
   hipError_t e = sta::launch_forward(a, p->variant, p->D, in_dtype == STA_F32, out_dtype == STA_F32,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? STA_OK : STA_ERR_HIP;
+}
+
+sta_status backward(const sta_plan *p, const void *q, const void *k, const void *v, const void *out,
+                    const void *dout, const float *lse, float *delta, void *dq, void *dk, void *dv,
+                    float scale, sta_dtype in_dtype, sta_dtype out_dtype, sta_dtype grad_dtype,
+                    sta_layout layout, void *stream) {
+  if (!p || !q || !k || !v || !out || !dout || !lse || !delta || !dq || !dk || !dv) return STA_ERR_ARG;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !valid_dtype(grad_dtype)) return STA_ERR_ARG;
+  if (layout != STA_LAYOUT_NATURAL && layout != STA_LAYOUT_TILE_MAJOR) return STA_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return STA_ERR_ARG;
+  if (!p->bwd_ok) return STA_ERR_UNSUPPORTED;
+  const size_t rows = (size_t)p->batch * p->heads * p->N;
+  const size_t elems = rows * p->D;
+  const size_t ib = elems * dtype_bytes(in_dtype), ob = elems * dtype_bytes(out_dtype);
+  const size_t gb = elems * dtype_bytes(grad_dtype), sb = rows * sizeof(float);
+  // Written buffers must not overlap each other or any input.
+  const void *written[] = {dq, dk, dv, delta};
+  const size_t wbytes[] = {gb, gb, gb, sb};
+  const void *read[] = {q, k, v, dout, out, lse};
+  const size_t rbytes[] = {ib, ib, ib, ib, ob, sb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(written[i], wbytes[i], read[j], rbytes[j])) return STA_ERR_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(written[i], wbytes[i], written[j], wbytes[j])) return STA_ERR_ARG;
+  }
+  DeviceTables t;
+  sta_status st = device_tables(p, &t);
+  if (st != STA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_bwd_delta(out, dout, delta, (int64_t)rows, p->D, out_dtype == STA_F32, in_dtype == STA_F32,
+                       s) != hipSuccess)
+    return STA_ERR_HIP;
+  BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.dout = dout;
+  a.lse = lse; a.delta = delta;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.base = layout == STA_LAYOUT_NATURAL ? t.base_nat : t.base_tm;
+  a.off = layout == STA_LAYOUT_NATURAL ? t.off_nat : t.off_tm;
+  a.heads = p->heads;
+  a.n_tiles = p->n_tiles;
+  a.V = p->V;
+  a.subs = p->bwd_subs;
+  a.N = p->N;
+  a.scale = scale;
+  a.sl2e = scale * 1.44269504088896340736f;
+  a.f32_out = grad_dtype == STA_F32;
+  const bool f32_in = in_dtype == STA_F32;
+  a.sched = t.sched_dq;
+  a.n_blocks = (int32_t)p->sched_dq.size();
+  a.list_off = t.kv_off;
+  a.list_idx = t.kv_idx;
+  a.max_list = p->max_nkv;
+  if (launch_bwd_dq(a, p->bwd_nw, p->D, f32_in, s) != hipSuccess) return STA_ERR_HIP;
+  a.sched = t.sched_dkdv;
+  a.n_blocks = (int32_t)p->sched_dkdv.size();
+  a.list_off = t.q_off;
+  a.list_idx = t.q_idx;
+  a.max_list = p->max_nq;
+  if (launch_bwd_dkdv(a, p->bwd_nw, p->D, f32_in, s) != hipSuccess) return STA_ERR_HIP;
+  return STA_OK;
+}
+
+}  // namespace
+}  // namespace sta
+
+extern "C" {
+
+sta_status sta_forward_plan(const sta_plan *p, const void *q, const void *k, const void *v,
+                            void *out, float scale, sta_dtype in_dtype, sta_dtype out_dtype,
+                            sta_layout layout, void *stream) {
+  return sta::forward(p, q, k, v, out, nullptr, scale, in_dtype, out_dtype, layout, stream);
+}
+
+sta_status sta_forward_plan_lse(const sta_plan *p, const void *q, const void *k, const void *v,
+                                void *out, float *lse, float scale, sta_dtype in_dtype,
+                                sta_dtype out_dtype, sta_layout layout, void *stream) {
+  if (!lse) return STA_ERR_ARG;
+  return sta::forward(p, q, k, v, out, lse, scale, in_dtype, out_dtype, layout, stream);
+}
+
+sta_status sta_backward_plan(const sta_plan *p, const void *q, const void *k, const void *v,
+                             const void *out, const void *dout, const float *lse, float *delta,
+                             void *dq, void *dk, void *dv, float scale, sta_dtype in_dtype,
+                             sta_dtype out_dtype, sta_dtype grad_dtype, sta_layout layout,
+                             void *stream) {
+  return sta::backward(p, q, k, v, out, dout, lse, delta, dq, dk, dv, scale, in_dtype, out_dtype,
+                       grad_dtype, layout, stream);
 }
 
 sta_status sta_forward(const void *q, const void *k, const void *v, void *out, int batch, int heads,

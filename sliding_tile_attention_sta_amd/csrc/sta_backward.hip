@@ -1,0 +1,535 @@
+// Sliding Tile Attention backward for gfx950 (MI355X).
+//
+// The pages fine-tune the video model with STA in place ("Fast Video
+// Generation with Sliding Tile Attention", arXiv 2502.04507, index page,
+// Abstract; gptget summary page, Summary and Experiments), so the operator is
+// trained through.  Its gradients are those of softmax attention restricted
+// to each query tile's window (chain rule of the forward definition):
+//
+//   P_ij  = exp(scale q_i.k_j - lse_i)        (lse from the forward)
+//   dv_j  = sum_i P_ij dO_i
+//   dS_ij = P_ij (dO_i.v_j - delta_i),        delta_i = dO_i . O_i
+//   dq_i  = scale sum_j dS_ij k_j,            dk_j = scale sum_i dS_ij q_i
+//
+// As in the forward, whole (query tile, key tile) pairs are attended or
+// skipped, so no kernel evaluates a mask.  Three kernels, no atomics (the
+// result does not depend on scheduling):
+//
+//   * delta: one fused multiply-add pass over dO and O (HBM bound).
+//   * dQ: a work group owns 32*NW queries of one (batch, head, query tile)
+//     and walks the key tiles of its window, 32 keys per step, like the
+//     forward: S^T = K Q^T and dP^T = V dO^T with the queries' Q and dO in
+//     VGPRs, then dQ^T += K^T dS^T with K^T read from LDS by the transposing
+//     ds_read_b64_tr_b16.
+//   * dK/dV: a work group owns 32*NW keys of one (batch, head, key tile) and
+//     walks the query tiles whose window holds that key tile (the inverse
+//     lists of the plan), 32 queries per step: S = Q K^T and dP = dO V^T with
+//     the keys' K and V in VGPRs, then dV^T += dO^T P and dK^T += Q^T dS with
+//     dO^T and Q^T read transposed from LDS.
+//
+// Every product runs on v_mfma_f32_16x16x32_f16 with fp32 accumulation.
+// P and dS are rounded to fp16 (11 significant bits against bf16's 8); Q and
+// K are the forward's bf16 values (fp32 inputs rounded to bf16 first, so
+// that the scores match the ones the forward's lse was taken over), widened
+// to fp16, which is exact inside the fp16 range; V and dO are converted to
+// fp16 (exact for bf16 values inside the range, nearest-even for fp32).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sta_device.h"
+#include "sta_internal.h"
+#include "sta_launch.h"
+
+namespace sta {
+namespace {
+
+constexpr int TB = kKeyBlock;  // tokens per pipeline step (keys for dQ, queries for dK/dV)
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Q and K chunks as fp16 holding the forward's bf16 values.
+template <bool F32>
+__device__ __forceinline__ uint4 score_f16(const Raw8<F32> &r) {
+  if constexpr (F32) {
+    Raw8<false> b;
+    b.x = as_bf16<true>(r);
+    return as_f16<false>(b);
+  } else {
+    return as_f16<false>(r);
+  }
+}
+
+__device__ __forceinline__ f16x8 lds_f16x8(const char *p) { return *reinterpret_cast<const f16x8 *>(p); }
+
+// Transposed 16x16x32 operand from a row-major fp16 [32][*] LDS block: lane
+// (g, l16) receives column col0 + l16 of rows 4g..4g+3 (slots 0..3) and
+// 16+4g..16+4g+3 (slots 4..7).  The same slot order is used for the
+// register operand it is multiplied with.
+__device__ __forceinline__ f16x8 lds_tr(const char *blk, int stride, int col0, int trow, int tcol) {
+  const lds_char *b = (const lds_char *)(blk) + (col0 + tcol) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(b + trow * stride));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(b + (trow + 16) * stride));
+  const f16x4 l = __builtin_bit_cast(f16x4, lo), h = __builtin_bit_cast(f16x4, hi);
+  return f16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+}
+
+__device__ __forceinline__ void store4(void *base, size_t e, const f32x4 &r, bool f32) {
+  if (f32) {
+    *reinterpret_cast<f32x4 *>(static_cast<char *>(base) + e * 4) = r;
+  } else {
+    bf16x4 b;
+    b[0] = (__bf16)r[0]; b[1] = (__bf16)r[1]; b[2] = (__bf16)r[2]; b[3] = (__bf16)r[3];
+    *reinterpret_cast<bf16x4 *>(static_cast<char *>(base) + e * 2) = b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// delta = rowsum(dO * O): D/8 lanes per row, 8 elements per lane; a
+// block-uniform grid-stride loop, so the shuffles always see whole rows.
+// ---------------------------------------------------------------------------
+template <int D, bool F32O, bool F32G>
+__global__ __launch_bounds__(256) void sta_bwd_delta_kernel(const void *o, const void *g, float *delta,
+                                                            int64_t rows) {
+  constexpr int LPR = D / 8;
+  const int64_t total = rows * LPR;
+  for (int64_t t0 = (int64_t)blockIdx.x * 256; t0 < total; t0 += (int64_t)gridDim.x * 256) {
+    const int64_t t = t0 + threadIdx.x;
+    const int64_t row = t / LPR;
+    const int c = (int)(t % LPR);
+    float acc = 0.f;
+    if (row < rows) {
+      const size_t e = (size_t)row * D + c * 8;
+      float ov[8], gv[8];
+      if constexpr (F32O) {
+        const float4 a = reinterpret_cast<const float4 *>(static_cast<const float *>(o) + e)[0];
+        const float4 b = reinterpret_cast<const float4 *>(static_cast<const float *>(o) + e)[1];
+        ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w; ov[4] = b.x; ov[5] = b.y; ov[6] = b.z; ov[7] = b.w;
+      } else {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(o) + e);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ov[i] = (float)a[i];
+      }
+      if constexpr (F32G) {
+        const float4 a = reinterpret_cast<const float4 *>(static_cast<const float *>(g) + e)[0];
+        const float4 b = reinterpret_cast<const float4 *>(static_cast<const float *>(g) + e)[1];
+        gv[0] = a.x; gv[1] = a.y; gv[2] = a.z; gv[3] = a.w; gv[4] = b.x; gv[5] = b.y; gv[6] = b.z; gv[7] = b.w;
+      } else {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(g) + e);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gv[i] = (float)a[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(ov[i], gv[i], acc);
+    }
+#pragma unroll
+    for (int s = 1; s < LPR; s <<= 1) acc += __shfl_xor(acc, s);
+    if (row < rows && c == 0) delta[row] = acc;
+  }
+}
+
+// Work item decode shared by both kernels: (batch*heads + h, tile, sub).
+struct Item {
+  int sub, tile, bh, h;
+};
+__device__ __forceinline__ Item decode(int item, const BwdArgs &a) {
+  Item it;
+  it.sub = item % a.subs;
+  const int rest = item / a.subs;
+  it.tile = rest % a.n_tiles;
+  it.bh = rest / a.n_tiles;
+  it.h = it.bh % a.heads;
+  return it;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: queries resident, key blocks streamed.
+// ---------------------------------------------------------------------------
+template <int D, int NW, bool F32IN>
+__global__ __launch_bounds__(NW * 64) void sta_bwd_dq_kernel(BwdArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int QPI = 32 * NW;
+  constexpr int STR = bwd_stride(D);
+  constexpr int ST = TB * STR;                   // bytes of one stage of one tensor
+  constexpr int CHUNKS = TB * D / 8;
+  constexpr int CPT = (CHUNKS + NT - 1) / NT;
+  static_assert(CHUNKS % NT == 0 || CHUNKS < NT, "chunk split");
+  constexpr int EB = F32IN ? 4 : 2;
+  constexpr int DC = D / 32;
+  constexpr int DB = D / 16;
+
+  // LDS: K stages 0/1, V stages 0/1, tile-local offsets, key-tile base rows.
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int *off_l = reinterpret_cast<int *>(smem + 4 * ST);
+  int *lb_l = off_l + a.V;
+
+  const int item = __builtin_amdgcn_readfirstlane(a.sched[blockIdx.x]);
+  if (item < 0) return;
+  const Item it = decode(item, a);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  const int l0 = __builtin_amdgcn_readfirstlane(a.list_off[it.h * a.n_tiles + it.tile]);
+  const int nl = __builtin_amdgcn_readfirstlane(a.list_off[it.h * a.n_tiles + it.tile + 1]) - l0;
+  for (int i = tid; i < a.V; i += NT) off_l[i] = a.off[i];
+  for (int i = tid; i < nl; i += NT) lb_l[i] = a.base[a.list_idx[l0 + i]];
+
+  const size_t plane = (size_t)it.bh * a.N;
+  const char *qg = static_cast<const char *>(a.q) + plane * D * EB;
+  const char *kg = static_cast<const char *>(a.k) + plane * D * EB;
+  const char *vg = static_cast<const char *>(a.v) + plane * D * EB;
+  const char *gg = static_cast<const char *>(a.dout) + plane * D * EB;
+  const int qbase = a.base[it.tile];
+  const int qloc0 = it.sub * QPI + wave * 32;
+  __syncthreads();
+
+  // Q and dO of the wave's 32 queries (B operands; lane: query 16j + l16).
+  f16x8 qf[2][DC], gf[2][DC];
+  float lse2[2], dl[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = qbase + off_l[qloc0 + 16 * j + l16];
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const size_t e = (size_t)row * D + 32 * c + 8 * g;
+      qf[j][c] = __builtin_bit_cast(f16x8, score_f16<F32IN>(load_raw<F32IN>(qg + e * EB)));
+      gf[j][c] = __builtin_bit_cast(f16x8, as_f16<F32IN>(load_raw<F32IN>(gg + e * EB)));
+    }
+    lse2[j] = a.lse[plane + row] * kLog2e;
+    dl[j] = a.delta[plane + row];
+  }
+
+  const int spt = a.V / TB;
+  const int nsteps = nl * spt;
+  Raw8<F32IN> rk[CPT], rv[CPT];
+  auto fetch = [&](int s) {
+    const int tb = lb_l[s / spt], u = s % spt;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS < NT && c >= CHUNKS) break;
+      const size_t e = (size_t)(tb + off_l[u * TB + c / (D / 8)]) * D + (c % (D / 8)) * 8;
+      rk[i] = load_raw<F32IN>(kg + e * EB);
+      rv[i] = load_raw<F32IN>(vg + e * EB);
+    }
+  };
+  auto stash = [&](int stage) {
+    char *ks = smem + stage * ST, *vs = smem + (2 + stage) * ST;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS < NT && c >= CHUNKS) break;
+      const int o = (c / (D / 8)) * STR + (c % (D / 8)) * 16;
+      *reinterpret_cast<uint4 *>(ks + o) = score_f16<F32IN>(rk[i]);
+      *reinterpret_cast<uint4 *>(vs + o) = as_f16<F32IN>(rv[i]);
+    }
+  };
+
+  f32x4 acc[DB][2];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sl2e = a.sl2e;
+  const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
+
+  if (nsteps > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const char *ks = smem + (s & 1) * ST, *vs = smem + (2 + (s & 1)) * ST;
+    // S^T = K Q^T, dP^T = V dO^T; lane: query 16j + l16, keys 16kb + 4g + r.
+    f32x4 st[2][2], dp[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        st[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const int o = (kb * 16 + l16) * STR + (32 * c + 8 * g) * 2;
+        const f16x8 ka = lds_f16x8(ks + o), va = lds_f16x8(vs + o);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          st[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[j][c], st[kb][j], 0, 0, 0);
+          dp[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, gf[j][c], dp[kb][j], 0, 0, 0);
+        }
+      }
+    // Next key block's loads, issued once the score accumulators are formed.
+    const bool more = s + 1 < nsteps;
+    if (more) fetch(s + 1);
+    // dS^T in fp16, slots: keys 4g + r (kb 0) and 16 + 4g + r (kb 1).
+    f16x8 dsf[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r], sl2e, -lse2[j]));
+          dsf[j][kb * 4 + r] = (_Float16)(p * (dp[kb][j][r] - dl[j]));
+        }
+    // dQ^T += K^T dS^T.
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const f16x8 kt = lds_tr(ks, STR, 16 * b, trow, tcol);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kt, dsf[j], acc[b][j], 0, 0, 0);
+    }
+    if (more) stash((s + 1) & 1);
+    __syncthreads();
+  }
+
+  // dQ = scale * acc; lane: query 16j + l16, d = 16b + 4g + r.
+  void *dq = static_cast<char *>(a.dq) + plane * D * (a.f32_out ? 4 : 2);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = qbase + off_l[qloc0 + 16 * j + l16];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) store4(dq, (size_t)row * D + 16 * b + 4 * g, acc[b][j] * a.scale, a.f32_out);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV: keys resident, query blocks streamed.
+// ---------------------------------------------------------------------------
+template <int D, int NW, bool F32IN>
+__global__ __launch_bounds__(NW * 64) void sta_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int KPI = 32 * NW;
+  constexpr int STR = bwd_stride(D);
+  constexpr int ST = TB * STR;
+  constexpr int CHUNKS = TB * D / 8;
+  constexpr int CPT = (CHUNKS + NT - 1) / NT;
+  static_assert(CHUNKS % NT == 0 || CHUNKS < NT, "chunk split");
+  static_assert(NT >= 2 * TB, "one thread per row statistic");
+  constexpr int EB = F32IN ? 4 : 2;
+  constexpr int DC = D / 32;
+  constexpr int DB = D / 16;
+
+  // LDS: Q stages 0/1, dO stages 0/1, lse*log2e stages 0/1 and delta stages
+  // 0/1 (32 floats each), tile-local offsets, query-tile base rows.
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float *stat = reinterpret_cast<float *>(smem + 4 * ST);   // [stage][lse2 | delta][32]
+  int *off_l = reinterpret_cast<int *>(stat + 4 * TB);
+  int *lb_l = off_l + a.V;
+
+  const int item = __builtin_amdgcn_readfirstlane(a.sched[blockIdx.x]);
+  if (item < 0) return;
+  const Item it = decode(item, a);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  const int l0 = __builtin_amdgcn_readfirstlane(a.list_off[it.h * a.n_tiles + it.tile]);
+  const int nl = __builtin_amdgcn_readfirstlane(a.list_off[it.h * a.n_tiles + it.tile + 1]) - l0;
+  for (int i = tid; i < a.V; i += NT) off_l[i] = a.off[i];
+  for (int i = tid; i < nl; i += NT) lb_l[i] = a.base[a.list_idx[l0 + i]];
+
+  const size_t plane = (size_t)it.bh * a.N;
+  const char *qg = static_cast<const char *>(a.q) + plane * D * EB;
+  const char *kg = static_cast<const char *>(a.k) + plane * D * EB;
+  const char *vg = static_cast<const char *>(a.v) + plane * D * EB;
+  const char *gg = static_cast<const char *>(a.dout) + plane * D * EB;
+  const float *lse = a.lse + plane, *delta = a.delta + plane;
+  const int kbase = a.base[it.tile];
+  const int kloc0 = it.sub * KPI + wave * 32;
+  __syncthreads();
+
+  // K and V of the wave's 32 keys (B operands; lane: key 16kb + l16).
+  f16x8 kf[2][DC], vf[2][DC];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = kbase + off_l[kloc0 + 16 * kb + l16];
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const size_t e = (size_t)row * D + 32 * c + 8 * g;
+      kf[kb][c] = __builtin_bit_cast(f16x8, score_f16<F32IN>(load_raw<F32IN>(kg + e * EB)));
+      vf[kb][c] = __builtin_bit_cast(f16x8, as_f16<F32IN>(load_raw<F32IN>(vg + e * EB)));
+    }
+  }
+
+  const int spt = a.V / TB;
+  const int nsteps = nl * spt;
+  Raw8<F32IN> rq[CPT], rg[CPT];
+  float rs = 0.f;   // threads 0..31: lse of query tid; 32..63: delta of query tid - 32
+  auto fetch = [&](int s) {
+    const int tb = lb_l[s / spt], u = s % spt;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS < NT && c >= CHUNKS) break;
+      const size_t e = (size_t)(tb + off_l[u * TB + c / (D / 8)]) * D + (c % (D / 8)) * 8;
+      rq[i] = load_raw<F32IN>(qg + e * EB);
+      rg[i] = load_raw<F32IN>(gg + e * EB);
+    }
+    if (tid < 2 * TB) {
+      const int row = tb + off_l[u * TB + (tid & (TB - 1))];
+      rs = tid < TB ? lse[row] * kLog2e : delta[row];
+    }
+  };
+  auto stash = [&](int stage) {
+    char *qs = smem + stage * ST, *gs = smem + (2 + stage) * ST;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS < NT && c >= CHUNKS) break;
+      const int o = (c / (D / 8)) * STR + (c % (D / 8)) * 16;
+      *reinterpret_cast<uint4 *>(qs + o) = score_f16<F32IN>(rq[i]);
+      *reinterpret_cast<uint4 *>(gs + o) = as_f16<F32IN>(rg[i]);
+    }
+    if (tid < 2 * TB) stat[stage * 2 * TB + tid] = rs;
+  };
+
+  f32x4 dk[DB][2], dv[DB][2];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      dk[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  const float sl2e = a.sl2e;
+  const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
+
+  if (nsteps > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int stg = s & 1;
+    const char *qs = smem + stg * ST, *gs = smem + (2 + stg) * ST;
+    const float *ls = stat + stg * 2 * TB, *ds = ls + TB;
+    // S = Q K^T, dP = dO V^T; lane: key 16kb + l16, queries 16j + 4g + r.
+    f32x4 sc[2][2], dp[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sc[j][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[j][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const int o = (j * 16 + l16) * STR + (32 * c + 8 * g) * 2;
+        const f16x8 qa = lds_f16x8(qs + o), ga = lds_f16x8(gs + o);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          sc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, kf[kb][c], sc[j][kb], 0, 0, 0);
+          dp[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ga, vf[kb][c], dp[j][kb], 0, 0, 0);
+        }
+      }
+    const bool more = s + 1 < nsteps;
+    if (more) fetch(s + 1);
+    // P and dS in fp16; slots 4j + r: queries 16j + 4g + r.
+    f16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f32x4 L = *reinterpret_cast<const f32x4 *>(ls + 16 * j + 4 * g);
+      const f32x4 Dl = *reinterpret_cast<const f32x4 *>(ds + 16 * j + 4 * g);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j][kb][r], sl2e, -L[r]));
+          pf[kb][4 * j + r] = (_Float16)p;
+          dsf[kb][4 * j + r] = (_Float16)(p * (dp[j][kb][r] - Dl[r]));
+        }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS.
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const f16x8 gt = lds_tr(gs, STR, 16 * b, trow, tcol);
+      const f16x8 qt = lds_tr(qs, STR, 16 * b, trow, tcol);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        dv[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(gt, pf[kb], dv[b][kb], 0, 0, 0);
+        dk[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qt, dsf[kb], dk[b][kb], 0, 0, 0);
+      }
+    }
+    if (more) stash(stg ^ 1);
+    __syncthreads();
+  }
+
+  // dK = scale * dk, dV = dv; lane: key 16kb + l16, d = 16b + 4g + r.
+  const size_t gb = plane * D * (a.f32_out ? 4 : 2);
+  void *dkp = static_cast<char *>(a.dk) + gb;
+  void *dvp = static_cast<char *>(a.dv) + gb;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = kbase + off_l[kloc0 + 16 * kb + l16];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const size_t e = (size_t)row * D + 16 * b + 4 * g;
+      store4(dkp, e, dk[b][kb] * a.scale, a.f32_out);
+      store4(dvp, e, dv[b][kb], a.f32_out);
+    }
+  }
+}
+
+template <typename K>
+hipError_t launch_lds(K kern, int blocks, int threads, size_t lds, const BwdArgs &a, hipStream_t s) {
+  if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int NW>
+hipError_t dq_one(const BwdArgs &a, bool f32_in, hipStream_t s) {
+  const size_t lds = (size_t)4 * TB * bwd_stride(D) + 4 * (a.V + a.max_list);
+  if (f32_in) return launch_lds(sta_bwd_dq_kernel<D, NW, true>, a.n_blocks, NW * 64, lds, a, s);
+  return launch_lds(sta_bwd_dq_kernel<D, NW, false>, a.n_blocks, NW * 64, lds, a, s);
+}
+
+template <int D, int NW>
+hipError_t dkdv_one(const BwdArgs &a, bool f32_in, hipStream_t s) {
+  const size_t lds = (size_t)4 * TB * bwd_stride(D) + 4 * 4 * TB + 4 * (a.V + a.max_list);
+  if (f32_in) return launch_lds(sta_bwd_dkdv_kernel<D, NW, true>, a.n_blocks, NW * 64, lds, a, s);
+  return launch_lds(sta_bwd_dkdv_kernel<D, NW, false>, a.n_blocks, NW * 64, lds, a, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_delta(const void *o, const void *dout, float *delta, int64_t rows, int head_dim,
+                            bool f32_o, bool f32_g, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t blocks = (rows * (head_dim / 8) + 255) / 256;
+  const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
+#define STA_DELTA(D, FO, FG) hipLaunchKernelGGL((sta_bwd_delta_kernel<D, FO, FG>), grid, dim3(256), 0, stream, o, dout, delta, rows)
+  if (head_dim == 128) {
+    if (f32_o) { if (f32_g) STA_DELTA(128, true, true); else STA_DELTA(128, true, false); }
+    else { if (f32_g) STA_DELTA(128, false, true); else STA_DELTA(128, false, false); }
+  } else {
+    if (f32_o) { if (f32_g) STA_DELTA(64, true, true); else STA_DELTA(64, true, false); }
+    else { if (f32_g) STA_DELTA(64, false, true); else STA_DELTA(64, false, false); }
+  }
+#undef STA_DELTA
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs &a, int nw, int head_dim, bool f32_in, hipStream_t stream) {
+  if (a.n_blocks <= 0) return hipSuccess;
+  if (head_dim == 128) return nw == 4 ? dq_one<128, 4>(a, f32_in, stream) : dq_one<128, 1>(a, f32_in, stream);
+  return nw == 4 ? dq_one<64, 4>(a, f32_in, stream) : dq_one<64, 1>(a, f32_in, stream);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs &a, int nw, int head_dim, bool f32_in, hipStream_t stream) {
+  if (a.n_blocks <= 0) return hipSuccess;
+  if (head_dim == 128) return nw == 4 ? dkdv_one<128, 4>(a, f32_in, stream) : dkdv_one<128, 1>(a, f32_in, stream);
+  return nw == 4 ? dkdv_one<64, 4>(a, f32_in, stream) : dkdv_one<64, 1>(a, f32_in, stream);
+}
+
+}  // namespace sta

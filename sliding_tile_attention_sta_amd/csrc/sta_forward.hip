@@ -361,12 +361,16 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   if (!grp_a) softmax();
   pvmm((nsteps - 1) & 1);
 
-  // ---- finalize: O = O^T / l, stored row-major ----------------------------
+  // ---- finalize: O = O^T / l, stored row-major; optionally the row
+  // log-sum-exp, ln(sum_j exp(scale s_j)) = (m * scale * log2(e) + log2(l)) * ln(2).
   char *og = reinterpret_cast<char *>(a.o) + (size_t)bh * a.N * D * (F32OUT ? 4 : 2);
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    const float inv = 1.f / swap_sum(l[j]);
+    const float lsum = swap_sum(l[j]);
+    const float inv = 1.f / lsum;
     const int row = qbase + off_l[qloc0 + 16 * j + l16];
+    if (a.lse != nullptr && g == 0)
+      a.lse[(size_t)bh * a.N + row] = (mb[j] + log2f(lsum)) * 0.69314718055994530942f;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       const f32x4 r = o[b][j] * inv;

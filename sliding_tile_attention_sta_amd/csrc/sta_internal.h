@@ -38,6 +38,16 @@ constexpr long long fwd_lds_bytes(int head_dim, long long tile_tokens, long long
 }
 constexpr long long kMaxLds = 160 * 1024;
 
+// The backward kernels stream blocks of 32 tokens (keys for dQ, queries for
+// dK/dV) through two-stage LDS rings of two fp16 tensors with the forward's
+// padded row stride, plus (dK/dV) the block's log-sum-exp and delta rows,
+// the tile-local row offsets and the item's tile base rows.
+constexpr int bwd_stride(int head_dim) { return 2 * head_dim + 32; }
+constexpr long long bwd_lds_bytes(int head_dim, long long tile_tokens, long long max_list) {
+  return 2LL * 2 * kKeyBlock * bwd_stride(head_dim) + 2LL * 2 * kKeyBlock * 4 +
+         4LL * (tile_tokens + max_list);
+}
+
 struct DeviceTables {
   int32_t *kv_off = nullptr;       // heads*n_tiles + 1
   int32_t *kv_idx = nullptr;       // sum of list lengths
@@ -46,6 +56,10 @@ struct DeviceTables {
   int32_t *off_nat = nullptr;      // tile_tokens: row offset of each tile-local token, natural order
   int32_t *base_tm = nullptr;      // n_tiles: tile * tile_tokens
   int32_t *off_tm = nullptr;       // tile_tokens: identity
+  int32_t *q_off = nullptr;        // heads*n_tiles + 1
+  int32_t *q_idx = nullptr;        // query tiles whose window holds each (head, key tile)
+  int32_t *sched_dq = nullptr;     // backward dQ work items in launch order (-1 = idle)
+  int32_t *sched_dkdv = nullptr;   // backward dK/dV work items in launch order (-1 = idle)
   void *block = nullptr;           // the single allocation holding all of the above
 };
 
@@ -68,6 +82,17 @@ struct sta_plan {
   int32_t variant = 0;
   int32_t qpi = 0;        // queries per work item
   int32_t subs = 0;       // work items per (b, head, query tile)
+
+  // Backward: inverse lists (query tiles whose window holds a key tile) and
+  // the schedules of the dQ and dK/dV kernels, whose items own
+  // 32 * bwd_nw tokens of one tile.
+  std::vector<int32_t> q_off;     // heads*n_tiles + 1
+  std::vector<int32_t> q_idx;
+  std::vector<int32_t> sched_dq, sched_dkdv;
+  int32_t max_nq = 0;     // longest inverse list
+  int32_t bwd_nw = 0;     // waves per backward work item
+  int32_t bwd_subs = 0;   // backward work items per (b, head, tile)
+  bool bwd_ok = false;    // the backward kernels' LDS fits
 
   mutable std::mutex mu;
   mutable std::map<int, sta::DeviceTables> dev;   // per HIP device ordinal

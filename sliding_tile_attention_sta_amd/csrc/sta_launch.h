@@ -20,11 +20,38 @@ struct FwdArgs {
   float sl2e;              // softmax scale * log2(e)
   int32_t n_blocks;        // length of sched
   int32_t max_nkv;         // longest key-tile list of any (head, query tile)
+  float *lse;              // NULL, or [batch, heads, N] row log-sum-exp (natural log)
 };
 
 // Launch the forward kernel.  variant: 0 generic, 1 384-query items.
 hipError_t launch_forward(const FwdArgs &a, int variant, int head_dim, bool f32_in, bool f32_out,
                           hipStream_t stream);
+
+struct BwdArgs {
+  const void *q, *k, *v, *dout;
+  const float *lse;        // [batch, heads, N], natural log
+  const float *delta;      // [batch, heads, N], rowsum(dO * O)
+  void *dq, *dk, *dv;
+  const int32_t *sched;    // work items in launch order (-1 = idle)
+  const int32_t *list_off; // dQ: key-tile lists per (head, query tile); dK/dV: query-tile lists
+  const int32_t *list_idx;
+  const int32_t *base;     // n_tiles: first token row of each tile in the tensors' layout
+  const int32_t *off;      // tile_tokens: row offset of each tile-local token
+  int32_t heads, n_tiles, V, subs;
+  int64_t N;
+  float scale;             // softmax scale
+  float sl2e;              // scale * log2(e)
+  int32_t n_blocks;        // length of sched
+  int32_t max_list;        // longest list
+  int32_t f32_out;         // gradients stored as fp32 (else bf16)
+};
+
+// delta[r] = sum_d dO[r, d] * O[r, d] for rows r < rows.
+hipError_t launch_bwd_delta(const void *o, const void *dout, float *delta, int64_t rows, int head_dim,
+                            bool f32_o, bool f32_g, hipStream_t stream);
+// dQ and dK/dV kernels; nw = waves per work item (32 tokens per wave).
+hipError_t launch_bwd_dq(const BwdArgs &a, int nw, int head_dim, bool f32_in, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs &a, int nw, int head_dim, bool f32_in, hipStream_t stream);
 
 struct ReorderArgs {
   const void *in;

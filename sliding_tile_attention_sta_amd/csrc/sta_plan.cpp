@@ -24,23 +24,24 @@ inline int window_start(int c, int w, int n) {
   return s;
 }
 
-// Work items in launch order.  Items are sorted by decreasing cost (number
-// of key tiles), cut into chunks of consecutive items, and each chunk goes to
-// the XCD with the least accumulated cost.  Blocks are dispatched to XCDs
-// round-robin (block b runs on XCD b % 8), so XCD x's queue is placed at
-// blocks x, x + 8, x + 16, ...  Within an XCD the hardware hands blocks to
-// free compute units in order, which is list scheduling of a
-// decreasing-cost list.  Chunks keep spatially adjacent query tiles of one
-// head on the same XCD, whose L2 then serves their overlapping windows.
-void build_schedule(sta_plan *p) {
-  const int64_t n_items = (int64_t)p->batch * p->heads * p->n_tiles * p->subs;
+// Work items in launch order.  Item code ((b * heads + h) * n_tiles + t) *
+// subs + sub; its cost is the length of list (h, t) in off.  Items are
+// sorted by decreasing cost, cut into chunks of consecutive items, and each
+// chunk goes to the XCD with the least accumulated cost.  Blocks are
+// dispatched to XCDs round-robin (block b runs on XCD b % 8), so XCD x's
+// queue is placed at blocks x, x + 8, x + 16, ...  Within an XCD the hardware
+// hands blocks to free compute units in order, which is list scheduling of a
+// decreasing-cost list.  Chunks keep spatially adjacent tiles of one head on
+// the same XCD, whose L2 then serves their overlapping windows.
+std::vector<int32_t> build_schedule(const sta_plan *p, const std::vector<int32_t> &off, int subs) {
+  const int64_t n_items = (int64_t)p->batch * p->heads * p->n_tiles * subs;
   std::vector<int64_t> order(n_items);
   std::iota(order.begin(), order.end(), 0);
   auto cost = [&](int64_t code) {
-    int64_t rest = code / p->subs;
-    int qt = (int)(rest % p->n_tiles);
+    int64_t rest = code / subs;
+    int t = (int)(rest % p->n_tiles);
     int h = (int)((rest / p->n_tiles) % p->heads);
-    return p->kv_off[h * p->n_tiles + qt + 1] - p->kv_off[h * p->n_tiles + qt];
+    return off[h * p->n_tiles + t + 1] - off[h * p->n_tiles + t];
   };
   std::stable_sort(order.begin(), order.end(),
                    [&](int64_t a, int64_t b) { return cost(a) > cost(b); });
@@ -58,9 +59,10 @@ void build_schedule(sta_plan *p) {
   }
   size_t len = 0;
   for (auto &q : queue) len = std::max(len, q.size());
-  p->sched.assign(len * kXcds, -1);
+  std::vector<int32_t> sched(len * kXcds, -1);
   for (int x = 0; x < kXcds; ++x)
-    for (size_t s = 0; s < queue[x].size(); ++s) p->sched[s * kXcds + x] = queue[x][s];
+    for (size_t s = 0; s < queue[x].size(); ++s) sched[s * kXcds + x] = queue[x][s];
+  return sched;
 }
 
 }  // namespace
@@ -148,7 +150,33 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
       const int lt = j / (tile[1] * tile[2]), ly = (j / tile[2]) % tile[1], lz = j % tile[2];
       p->off_nat[j] = (lt * H + ly) * W + lz;
     }
-    build_schedule(p);
+    p->sched = build_schedule(p, p->kv_off, p->subs);
+
+    // Backward: the inverse of the key-tile lists (query tiles, ascending),
+    // per head, and the two backward schedules.
+    p->q_off.assign((size_t)heads * p->n_tiles + 1, 0);
+    {
+      std::vector<std::vector<int32_t>> inv(p->n_tiles);
+      for (int h = 0; h < heads; ++h) {
+        for (auto &v : inv) v.clear();
+        for (int qt = 0; qt < p->n_tiles; ++qt) {
+          const size_t i = (size_t)h * p->n_tiles + qt;
+          for (int32_t e = p->kv_off[i]; e < p->kv_off[i + 1]; ++e) inv[p->kv_idx[e]].push_back(qt);
+        }
+        for (int kt = 0; kt < p->n_tiles; ++kt) {
+          p->q_idx.insert(p->q_idx.end(), inv[kt].begin(), inv[kt].end());
+          p->q_off[(size_t)h * p->n_tiles + kt + 1] = (int32_t)p->q_idx.size();
+          p->max_nq = std::max(p->max_nq, (int32_t)inv[kt].size());
+        }
+      }
+    }
+    p->bwd_nw = p->V % 128 == 0 ? 4 : 1;
+    p->bwd_subs = p->V / (32 * p->bwd_nw);
+    p->bwd_ok = bwd_lds_bytes(head_dim, p->V, std::max(p->max_nkv, p->max_nq)) <= kMaxLds;
+    if (p->bwd_ok) {
+      p->sched_dq = build_schedule(p, p->kv_off, p->bwd_subs);
+      p->sched_dkdv = build_schedule(p, p->q_off, p->bwd_subs);
+    }
   } catch (const std::bad_alloc &) {
     delete p;
     return STA_ERR_ALLOC;
@@ -187,6 +215,10 @@ sta_status sta_plan_get_info(const sta_plan *p, sta_plan_info *info) {
   info->work_items = (int64_t)p->sched.size();
   info->queries_per_item = p->qpi;
   info->kernel_variant = p->variant;
+  info->bwd_supported = p->bwd_ok ? 1 : 0;
+  info->bwd_tokens_per_item = 32 * p->bwd_nw;
+  info->bwd_items_dq = (int64_t)p->sched_dq.size();
+  info->bwd_items_dkdv = (int64_t)p->sched_dkdv.size();
   return STA_OK;
 }
 
@@ -208,6 +240,28 @@ sta_status sta_plan_kv_tiles(const sta_plan *p, int head, int q_tile, int32_t *o
   if (!out && cap > 0) return STA_ERR_ARG;
   for (int j = 0; j < cap && j < (int)list.size(); ++j) out[j] = list[j];
   return (int)list.size() > cap ? STA_ERR_ARG : STA_OK;
+}
+
+sta_status sta_plan_q_tiles(const sta_plan *p, int head, int kv_tile, int32_t *out, int cap,
+                            int *count) {
+  if (!p || !count || head < 0 || head >= p->heads || kv_tile < 0 || kv_tile >= p->n_tiles)
+    return STA_ERR_ARG;
+  const size_t i = (size_t)head * p->n_tiles + kv_tile;
+  const int n = p->q_off[i + 1] - p->q_off[i];
+  *count = n;
+  if (!out && cap > 0) return STA_ERR_ARG;
+  for (int j = 0; j < cap && j < n; ++j) out[j] = p->q_idx[p->q_off[i] + j];
+  return n > cap ? STA_ERR_ARG : STA_OK;
+}
+
+sta_status sta_plan_schedule_bwd(const sta_plan *p, int which, int32_t *out, int64_t cap,
+                                 int64_t *count) {
+  if (!p || !count || (which != 0 && which != 1)) return STA_ERR_ARG;
+  const std::vector<int32_t> &s = which == 0 ? p->sched_dq : p->sched_dkdv;
+  *count = (int64_t)s.size();
+  if (cap < *count || (!out && *count > 0)) return STA_ERR_ARG;
+  if (!s.empty()) std::memcpy(out, s.data(), s.size() * sizeof(int32_t));
+  return STA_OK;
 }
 
 sta_status sta_plan_schedule(const sta_plan *p, int32_t *out, int64_t cap, int64_t *count) {

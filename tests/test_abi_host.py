@@ -188,3 +188,82 @@ def test_forward_argument_errors_precede_device_work():
     assert lib.sta_forward(q, k, v, o, 1, 2, 6, 16, 16, t, win, 80, 0.125, 0, 1, 0, None) == L.STA_ERR_UNSUPPORTED
     assert lib.sta_forward(q, k, v, o, 1, 2, 6, 16, 16, None, win, 64, 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
     assert lib.sta_clear_plan_cache() == L.STA_OK
+
+
+# ---------------------------------------------------------------------------
+# Backward plan tables
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "small", "720p", "mixed"])
+def test_inverse_lists_match_oracle(name):
+    from oracle import sta_oracle_bwd as OB
+    w = WORKLOADS[name]
+    p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    grid = O.tile_grid(w.video, w.tile)
+    nT, nH, nW = grid
+    heads = range(w.heads) if w.heads <= 8 else range(0, 4)
+    for h in heads:
+        for kt in range(0, nT * nH * nW, 5 if nT * nH * nW > 64 else 1):
+            c = (kt // (nH * nW), (kt // nW) % nH, kt % nW)
+            want = [(a * nH + b) * nW + cc for a, b, cc in OB.query_tiles_seeing(c, w.windows[h], grid)]
+            assert p.q_tiles(h, kt) == want
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "720p", "mixed"])
+def test_backward_schedules_cover_every_item_once(name):
+    w = WORKLOADS[name]
+    p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    info = p.info
+    assert info.bwd_supported == 1
+    assert info.tile_tokens % info.bwd_tokens_per_item == 0
+    subs = info.tile_tokens // info.bwd_tokens_per_item
+    n_items = w.batch * w.heads * info.n_tiles * subs
+    for which, count in ((0, info.bwd_items_dq), (1, info.bwd_items_dkdv)):
+        s = p.schedule_bwd(which).numpy()
+        assert len(s) == count and len(s) % 8 == 0
+        assert sorted(s[s >= 0].tolist()) == list(range(n_items))
+        assert (s[s < 0] == -1).all()
+    # the dK/dV items are ordered by the length of their inverse list
+    s = p.schedule_bwd(1).numpy()
+    for x in range(8):
+        lens = []
+        for c in s[x::8].tolist():
+            if c >= 0:
+                rest = c // subs
+                lens.append(len(p.q_tiles((rest // info.n_tiles) % w.heads, rest % info.n_tiles)))
+        assert lens == sorted(lens, reverse=True)
+
+
+def test_backward_argument_errors_precede_device_work():
+    p = api.Plan(1, 2, (6, 16, 16), (2, 4, 4), [(3, 3, 3)], 64)
+    lib = L.lib()
+    P = ctypes.c_void_p
+    q, k, v, o, g = P(1 << 40), P(2 << 40), P(3 << 40), P(4 << 40), P(5 << 40)
+    lse, dl, dq, dk, dv = P(6 << 40), P(7 << 40), P(8 << 40), P(9 << 40), P(10 << 40)
+    ok = (p.handle, q, k, v, o, g, lse, dl, dq, dk, dv, 0.125, 0, 1, 1, 0, None)
+
+    def call(**kw):
+        args = list(ok)
+        names = ["plan", "q", "k", "v", "o", "g", "lse", "dl", "dq", "dk", "dv", "scale", "in_dt",
+                 "out_dt", "grad_dt", "layout", "stream"]
+        for key, val in kw.items():
+            args[names.index(key)] = val
+        return lib.sta_backward_plan(*args)
+
+    for name in ["plan", "q", "k", "v", "o", "g", "lse", "dl", "dq", "dk", "dv"]:
+        assert call(**{name: None}) == L.STA_ERR_ARG, name
+    assert call(scale=0.0) == L.STA_ERR_ARG
+    assert call(scale=float("inf")) == L.STA_ERR_ARG
+    assert call(in_dt=3) == L.STA_ERR_ARG
+    assert call(out_dt=3) == L.STA_ERR_ARG
+    assert call(grad_dt=3) == L.STA_ERR_ARG
+    assert call(layout=2) == L.STA_ERR_ARG
+    # written buffers overlapping an input or each other
+    assert call(dq=P((1 << 40) + 64)) == L.STA_ERR_ARG
+    assert call(dv=P((4 << 40) + 64)) == L.STA_ERR_ARG
+    assert call(dk=P((8 << 40) + 64)) == L.STA_ERR_ARG
+    assert call(dl=P((6 << 40) + 4)) == L.STA_ERR_ARG
+    assert call(dl=P((10 << 40) + 4)) == L.STA_ERR_ARG
+    assert lib.sta_forward_plan_lse(p.handle, q, k, v, o, None, 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_forward_plan_lse(p.handle, q, k, v, o, P((3 << 40) + 8), 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
+    assert lib.sta_forward_plan_lse(None, q, k, v, o, lse, 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
