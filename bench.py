@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
+                    help="forward (the metric line) or backward (delta + dQ + dK/dV kernels)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -111,6 +113,46 @@ def _cpu_model():
     return "unknown"
 
 
+def backward(args, w, plan, q, k, v, stream):
+    """One step = the STA backward call (delta, dQ and dK/dV kernels) for
+    the forward's output and row log-sum-exp, computed once beforehand."""
+    import torch
+    from sliding_tile_attention_sta_amd import api
+    from sliding_tile_attention_sta_amd.synthetic import make_grad_out
+
+    g = make_grad_out(w, q.device)
+    out, lse = api.sta_forward_plan(plan, q, k, v, scale=w.scale, out_dtype=torch.float32, lse=True)
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    delta = torch.empty_like(lse)
+
+    def step():
+        api.sta_backward_plan(plan, q, k, v, out, g, lse, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                              delta=delta, stream=stream)
+
+    ms = timed(step, args.steps, args.warmup, stream)
+    fwd_flops = plan.flops
+    # Algorithmic backward FLOPs: five products per attended tile pair
+    # (Q K^T recomputed, dO V^T, P^T dO, dS K, dS^T Q), 2.5x the forward's.
+    # The two kernels execute seven (dQ recomputes Q K^T and dO V^T).
+    flops = 2.5 * fwd_flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": "STA bwd ms + achieved TFLOP/s (algorithmic, 2.5x forward FLOPs)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": w.name, "video": list(w.video), "tile": list(w.tile),
+                   "windows": sorted({tuple(x) for x in w.windows}), "heads": w.heads,
+                   "head_dim": w.head_dim, "batch": w.batch, "layout": "natural",
+                   "in_dtype": "bf16", "grad_dtype": "f32",
+                   "products": "fp16 MFMA, fp32 accumulate", "flops_per_step": flops,
+                   "executed_flops_per_step": 3.5 * fwd_flops},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "whole backward call (delta + dQ + dK/dV)"},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -139,6 +181,9 @@ def main():
     stream = torch.cuda.current_stream()
     q, k, v = make_qkv(w, dev)
     plan = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    if args.which == "backward":
+        print(json.dumps(backward(args, w, plan, q, k, v, stream)), flush=True)
+        return
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     flops = plan.flops
 

@@ -297,12 +297,24 @@ __global__ __launch_bounds__(NW * 64) void sta_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV: keys resident, query blocks streamed.
+// dK/dV: keys resident, query blocks streamed, each 32-key group split over a
+// pair of waves on one SIMD.  Holding K, V, dK and dV of 32 keys takes about
+// 316 registers per wave, which leaves one wave per SIMD and nothing to
+// overlap a wave's exp work with; split, each wave needs about 150:
+//   wave A (waves 0..NP-1): K and dV.  Step s: S = Q K^T, P = exp(S - lse),
+//     P to LDS for its partner, dV^T += dO^T P.
+//   wave B (waves NP..2NP-1): V and dK, one step behind.  Step s: dP = dO
+//     V^T of block s-1, P of block s-1 from LDS, dS = P (dP - delta),
+//     dK^T += Q^T dS.
+// A's exp work then overlaps B's MFMAs and the other way round.  Query
+// blocks pass through a three-stage LDS ring (A reads block s while B reads
+// block s-1 and block s+1 is written), the P exchange through a two-stage
+// buffer; one barrier per step.
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool F32IN>
-__global__ __launch_bounds__(NW * 64) void sta_bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int KPI = 32 * NW;
+template <int D, int NP, bool F32IN>
+__global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NT = NP * 128;
+  constexpr int KPI = 32 * NP;
   constexpr int STR = bwd_stride(D);
   constexpr int ST = TB * STR;
   constexpr int CHUNKS = TB * D / 8;
@@ -312,12 +324,15 @@ __global__ __launch_bounds__(NW * 64) void sta_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int EB = F32IN ? 4 : 2;
   constexpr int DC = D / 32;
   constexpr int DB = D / 16;
+  constexpr int PB = NP * 2 * 64 * 16;            // bytes of one P exchange stage
 
-  // LDS: Q stages 0/1, dO stages 0/1, lse*log2e stages 0/1 and delta stages
-  // 0/1 (32 floats each), tile-local offsets, query-tile base rows.
+  // LDS: Q stages 0..2, dO stages 0..2, row statistics [stage][lse*log2e |
+  // delta][32], P exchange stages 0/1 [pair][kb][lane] (16 B), tile-local
+  // offsets, query-tile base rows.
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  float *stat = reinterpret_cast<float *>(smem + 4 * ST);   // [stage][lse2 | delta][32]
-  int *off_l = reinterpret_cast<int *>(stat + 4 * TB);
+  float *stat = reinterpret_cast<float *>(smem + 6 * ST);
+  char *pbuf = reinterpret_cast<char *>(stat + 3 * 2 * TB);
+  int *off_l = reinterpret_cast<int *>(pbuf + 2 * PB);
   int *lb_l = off_l + a.V;
 
   const int item = __builtin_amdgcn_readfirstlane(a.sched[blockIdx.x]);
@@ -325,6 +340,8 @@ __global__ __launch_bounds__(NW * 64) void sta_bwd_dkdv_kernel(BwdArgs a) {
   const Item it = decode(item, a);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
+  const bool wa = wave < NP;            // wave-uniform
+  const int pair = wa ? wave : wave - NP;
 
   const int l0 = __builtin_amdgcn_readfirstlane(a.list_off[it.h * a.n_tiles + it.tile]);
   const int nl = __builtin_amdgcn_readfirstlane(a.list_off[it.h * a.n_tiles + it.tile + 1]) - l0;
@@ -333,24 +350,28 @@ __global__ __launch_bounds__(NW * 64) void sta_bwd_dkdv_kernel(BwdArgs a) {
 
   const size_t plane = (size_t)it.bh * a.N;
   const char *qg = static_cast<const char *>(a.q) + plane * D * EB;
-  const char *kg = static_cast<const char *>(a.k) + plane * D * EB;
-  const char *vg = static_cast<const char *>(a.v) + plane * D * EB;
   const char *gg = static_cast<const char *>(a.dout) + plane * D * EB;
   const float *lse = a.lse + plane, *delta = a.delta + plane;
   const int kbase = a.base[it.tile];
-  const int kloc0 = it.sub * KPI + wave * 32;
+  const int kloc0 = it.sub * KPI + pair * 32;
   __syncthreads();
 
-  // K and V of the wave's 32 keys (B operands; lane: key 16kb + l16).
-  f16x8 kf[2][DC], vf[2][DC];
+  // The pair's 32 keys as B operands (lane: key 16kb + l16): K for wave A,
+  // V for wave B.
+  f16x8 frag[2][DC];
+  {
+    const char *src = static_cast<const char *>(wa ? a.k : a.v) + plane * D * EB;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int row = kbase + off_l[kloc0 + 16 * kb + l16];
+    for (int kb = 0; kb < 2; ++kb) {
+      const int row = kbase + off_l[kloc0 + 16 * kb + l16];
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const size_t e = (size_t)row * D + 32 * c + 8 * g;
-      kf[kb][c] = __builtin_bit_cast(f16x8, score_f16<F32IN>(load_raw<F32IN>(kg + e * EB)));
-      vf[kb][c] = __builtin_bit_cast(f16x8, as_f16<F32IN>(load_raw<F32IN>(vg + e * EB)));
+      for (int c = 0; c < DC; ++c) {
+        const Raw8<F32IN> r = load_raw<F32IN>(src + ((size_t)row * D + 32 * c + 8 * g) * EB);
+        if constexpr (F32IN)
+          frag[kb][c] = __builtin_bit_cast(f16x8, wa ? score_f16<true>(r) : as_f16<true>(r));
+        else
+          frag[kb][c] = __builtin_bit_cast(f16x8, as_f16<false>(r));
+      }
     }
   }
 
@@ -374,7 +395,7 @@ __global__ __launch_bounds__(NW * 64) void sta_bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   auto stash = [&](int stage) {
-    char *qs = smem + stage * ST, *gs = smem + (2 + stage) * ST;
+    char *qs = smem + stage * ST, *gs = smem + (3 + stage) * ST;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
@@ -386,14 +407,12 @@ __global__ __launch_bounds__(NW * 64) void sta_bwd_dkdv_kernel(BwdArgs a) {
     if (tid < 2 * TB) stat[stage * 2 * TB + tid] = rs;
   };
 
-  f32x4 dk[DB][2], dv[DB][2];
+  // dV^T (wave A) or dK^T / scale (wave B); lane: key 16kb + l16, d 16b + 4g + r.
+  f32x4 acc[DB][2];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      dk[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dv[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int kb = 0; kb < 2; ++kb) acc[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sl2e = a.sl2e;
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
 
@@ -402,76 +421,88 @@ __global__ __launch_bounds__(NW * 64) void sta_bwd_dkdv_kernel(BwdArgs a) {
     stash(0);
   }
   __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int stg = s & 1;
-    const char *qs = smem + stg * ST, *gs = smem + (2 + stg) * ST;
-    const float *ls = stat + stg * 2 * TB, *ds = ls + TB;
-    // S = Q K^T, dP = dO V^T; lane: key 16kb + l16, queries 16j + 4g + r.
-    f32x4 sc[2][2], dp[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sc[j][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[j][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const int o = (j * 16 + l16) * STR + (32 * c + 8 * g) * 2;
-        const f16x8 qa = lds_f16x8(qs + o), ga = lds_f16x8(gs + o);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          sc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, kf[kb][c], sc[j][kb], 0, 0, 0);
-          dp[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ga, vf[kb][c], dp[j][kb], 0, 0, 0);
-        }
-      }
+  // Iteration s: wave A works on block s (s < nsteps), wave B on block s-1
+  // (s >= 1).  stage(x) = x mod 3.
+  int st_cur = 0;                        // stage of block s
+  for (int s = 0; s <= nsteps; ++s) {
+    const int st_prev = st_cur == 0 ? 2 : st_cur - 1;
+    const int st_next = st_cur == 2 ? 0 : st_cur + 1;
     const bool more = s + 1 < nsteps;
     if (more) fetch(s + 1);
-    // P and dS in fp16; slots 4j + r: queries 16j + 4g + r.
-    f16x8 pf[2], dsf[2];
+    const bool active = wa ? s < nsteps : s >= 1;
+    if (active) {
+      const int stg = wa ? st_cur : st_prev;
+      const char *qs = smem + stg * ST, *gs = smem + (3 + stg) * ST;
+      const float *ls = stat + stg * 2 * TB;
+      char *pex = pbuf + ((wa ? s : s - 1) & 1) * PB + pair * 2 * 64 * 16 + lane * 16;
+      // A: S = Q K^T; B: dP = dO V^T.  Lane: key 16kb + l16, queries 16j + 4g + r.
+      const char *rows = wa ? qs : gs;
+      f32x4 t[2][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const f32x4 L = *reinterpret_cast<const f32x4 *>(ls + 16 * j + 4 * g);
-      const f32x4 Dl = *reinterpret_cast<const f32x4 *>(ds + 16 * j + 4 * g);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) t[j][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j][kb][r], sl2e, -L[r]));
-          pf[kb][4 * j + r] = (_Float16)p;
-          dsf[kb][4 * j + r] = (_Float16)(p * (dp[j][kb][r] - Dl[r]));
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          const f16x8 x = lds_f16x8(rows + (j * 16 + l16) * STR + (32 * c + 8 * g) * 2);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            t[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, frag[kb][c], t[j][kb], 0, 0, 0);
         }
-    }
-    // dV^T += dO^T P, dK^T += Q^T dS.
+      // Slots 4j + r of each 16-key block: queries 16j + 4g + r.
+      f16x8 w[2];
+      if (wa) {
+        // P = exp2(S scale log2(e) - lse log2(e)), to registers and LDS.
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const f16x8 gt = lds_tr(gs, STR, 16 * b, trow, tcol);
-      const f16x8 qt = lds_tr(qs, STR, 16 * b, trow, tcol);
+        for (int j = 0; j < 2; ++j) {
+          const f32x4 L = *reinterpret_cast<const f32x4 *>(ls + 16 * j + 4 * g);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        dv[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(gt, pf[kb], dv[b][kb], 0, 0, 0);
-        dk[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qt, dsf[kb], dk[b][kb], 0, 0, 0);
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              w[kb][4 * j + r] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(t[j][kb][r], sl2e, -L[r]));
+        }
+        *reinterpret_cast<f16x8 *>(pex) = w[0];
+        *reinterpret_cast<f16x8 *>(pex + 64 * 16) = w[1];
+      } else {
+        // dS = P (dP - delta), P from the partner.
+        const f16x8 p0 = *reinterpret_cast<const f16x8 *>(pex);
+        const f16x8 p1 = *reinterpret_cast<const f16x8 *>(pex + 64 * 16);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const f32x4 Dl = *reinterpret_cast<const f32x4 *>(ls + TB + 16 * j + 4 * g);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            w[0][4 * j + r] = (_Float16)((float)p0[4 * j + r] * (t[j][0][r] - Dl[r]));
+            w[1][4 * j + r] = (_Float16)((float)p1[4 * j + r] * (t[j][1][r] - Dl[r]));
+          }
+        }
+      }
+      // A: dV^T += dO^T P; B: dK^T += Q^T dS.
+      const char *tsrc = wa ? gs : qs;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const f16x8 x = lds_tr(tsrc, STR, 16 * b, trow, tcol);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) acc[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, w[kb], acc[b][kb], 0, 0, 0);
       }
     }
-    if (more) stash(stg ^ 1);
+    if (more) stash(st_next);
     __syncthreads();
+    st_cur = st_next;
   }
 
-  // dK = scale * dk, dV = dv; lane: key 16kb + l16, d = 16b + 4g + r.
+  // dV = acc (wave A), dK = scale * acc (wave B).
   const size_t gb = plane * D * (a.f32_out ? 4 : 2);
-  void *dkp = static_cast<char *>(a.dk) + gb;
-  void *dvp = static_cast<char *>(a.dv) + gb;
+  void *dst = static_cast<char *>(wa ? a.dv : a.dk) + gb;
+  const float mul = wa ? 1.f : a.scale;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int row = kbase + off_l[kloc0 + 16 * kb + l16];
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const size_t e = (size_t)row * D + 16 * b + 4 * g;
-      store4(dkp, e, dk[b][kb] * a.scale, a.f32_out);
-      store4(dvp, e, dv[b][kb], a.f32_out);
-    }
+    for (int b = 0; b < DB; ++b) store4(dst, (size_t)row * D + 16 * b + 4 * g, acc[b][kb] * mul, a.f32_out);
   }
 }
 
@@ -494,11 +525,12 @@ hipError_t dq_one(const BwdArgs &a, bool f32_in, hipStream_t s) {
   return launch_lds(sta_bwd_dq_kernel<D, NW, false>, a.n_blocks, NW * 64, lds, a, s);
 }
 
-template <int D, int NW>
+template <int D, int NP>
 hipError_t dkdv_one(const BwdArgs &a, bool f32_in, hipStream_t s) {
-  const size_t lds = (size_t)4 * TB * bwd_stride(D) + 4 * 4 * TB + 4 * (a.V + a.max_list);
-  if (f32_in) return launch_lds(sta_bwd_dkdv_kernel<D, NW, true>, a.n_blocks, NW * 64, lds, a, s);
-  return launch_lds(sta_bwd_dkdv_kernel<D, NW, false>, a.n_blocks, NW * 64, lds, a, s);
+  const size_t lds = (size_t)6 * TB * bwd_stride(D) + 4 * 6 * TB + 2 * NP * 2 * 64 * 16 +
+                     4 * (a.V + a.max_list);
+  if (f32_in) return launch_lds(sta_bwd_dkdv_kernel<D, NP, true>, a.n_blocks, NP * 128, lds, a, s);
+  return launch_lds(sta_bwd_dkdv_kernel<D, NP, false>, a.n_blocks, NP * 128, lds, a, s);
 }
 
 }  // namespace

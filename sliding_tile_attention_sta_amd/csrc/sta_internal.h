@@ -39,12 +39,14 @@ constexpr long long fwd_lds_bytes(int head_dim, long long tile_tokens, long long
 constexpr long long kMaxLds = 160 * 1024;
 
 // The backward kernels stream blocks of 32 tokens (keys for dQ, queries for
-// dK/dV) through two-stage LDS rings of two fp16 tensors with the forward's
-// padded row stride, plus (dK/dV) the block's log-sum-exp and delta rows,
-// the tile-local row offsets and the item's tile base rows.
+// dK/dV) through LDS rings of two fp16 tensors with the forward's padded row
+// stride: two stages for dQ, three for dK/dV, which also keeps the blocks'
+// log-sum-exp and delta rows and two stages of the probability exchange
+// between its wave pairs (up to 4 pairs x 2 KiB).  Both keep the tile-local
+// row offsets and the item's tile base rows.  The dK/dV layout is the larger.
 constexpr int bwd_stride(int head_dim) { return 2 * head_dim + 32; }
 constexpr long long bwd_lds_bytes(int head_dim, long long tile_tokens, long long max_list) {
-  return 2LL * 2 * kKeyBlock * bwd_stride(head_dim) + 2LL * 2 * kKeyBlock * 4 +
+  return 3LL * 2 * kKeyBlock * bwd_stride(head_dim) + 3LL * 2 * kKeyBlock * 4 + 2LL * 4 * 2048 +
          4LL * (tile_tokens + max_list);
 }
 
