@@ -73,7 +73,8 @@ typedef struct {
   int32_t queries_per_item; /* query tokens per work item */
   int32_t kernel_variant;   /* 0 = generic (32 queries / item), 1 = 384-query items */
   int32_t bwd_supported;    /* 1 if sta_backward_plan accepts this plan */
-  int32_t bwd_tokens_per_item; /* queries (dQ) or keys (dK/dV) per backward work item */
+  int32_t bwd_queries_per_item; /* queries per dQ work item */
+  int32_t bwd_keys_per_item;    /* keys per dK/dV work item */
   int64_t bwd_items_dq;     /* launched dQ work items (including idle padding) */
   int64_t bwd_items_dkdv;   /* launched dK/dV work items (including idle padding) */
 } sta_plan_info;
@@ -121,9 +122,9 @@ sta_status sta_plan_q_tiles(const sta_plan *plan, int head, int kv_tile, int32_t
 sta_status sta_plan_schedule(const sta_plan *plan, int32_t *out, int64_t cap, int64_t *count);
 
 /* The backward schedules, same conventions: which = 0 for the dQ kernel
- * (code ((b * heads + h) * n_tiles + q_tile) * subs + sub), 1 for the dK/dV
- * kernel (the same with the key tile), subs = tile_tokens /
- * bwd_tokens_per_item.  Empty when bwd_supported is 0. */
+ * (code ((b * heads + h) * n_tiles + q_tile) * subs + sub, subs =
+ * tile_tokens / bwd_queries_per_item), 1 for the dK/dV kernel (the same
+ * with the key tile and bwd_keys_per_item).  Empty when bwd_supported is 0. */
 sta_status sta_plan_schedule_bwd(const sta_plan *plan, int which, int32_t *out, int64_t cap,
                                  int64_t *count);
 

@@ -25,7 +25,8 @@ class PlanInfo(ctypes.Structure):
         ("tokens", ctypes.c_int64), ("pairs", ctypes.c_int64), ("flops", ctypes.c_double),
         ("work_items", ctypes.c_int64), ("queries_per_item", ctypes.c_int32),
         ("kernel_variant", ctypes.c_int32), ("bwd_supported", ctypes.c_int32),
-        ("bwd_tokens_per_item", ctypes.c_int32), ("bwd_items_dq", ctypes.c_int64),
+        ("bwd_queries_per_item", ctypes.c_int32), ("bwd_keys_per_item", ctypes.c_int32),
+        ("bwd_items_dq", ctypes.c_int64),
         ("bwd_items_dkdv", ctypes.c_int64),
     ]
 

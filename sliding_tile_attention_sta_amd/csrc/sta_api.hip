@@ -215,7 +215,6 @@ sta_status backward(const sta_plan *p, const void *q, const void *k, const void 
   a.heads = p->heads;
   a.n_tiles = p->n_tiles;
   a.V = p->V;
-  a.subs = p->bwd_subs;
   a.N = p->N;
   a.scale = scale;
   a.sl2e = scale * 1.44269504088896340736f;
@@ -226,13 +225,15 @@ sta_status backward(const sta_plan *p, const void *q, const void *k, const void 
   a.list_off = t.kv_off;
   a.list_idx = t.kv_idx;
   a.max_list = p->max_nkv;
-  if (launch_bwd_dq(a, p->bwd_nw, p->D, f32_in, s) != hipSuccess) return STA_ERR_HIP;
+  a.subs = p->bwd_q_subs;
+  if (launch_bwd_dq(a, p->bwd_q_waves, p->D, f32_in, s) != hipSuccess) return STA_ERR_HIP;
   a.sched = t.sched_dkdv;
   a.n_blocks = (int32_t)p->sched_dkdv.size();
   a.list_off = t.q_off;
   a.list_idx = t.q_idx;
   a.max_list = p->max_nq;
-  if (launch_bwd_dkdv(a, p->bwd_nw, p->D, f32_in, s) != hipSuccess) return STA_ERR_HIP;
+  a.subs = p->bwd_k_subs;
+  if (launch_bwd_dkdv(a, p->bwd_k_pairs, p->D, f32_in, s) != hipSuccess) return STA_ERR_HIP;
   return STA_OK;
 }
 

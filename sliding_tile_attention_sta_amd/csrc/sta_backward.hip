@@ -558,10 +558,16 @@ hipError_t launch_bwd_dq(const BwdArgs &a, int nw, int head_dim, bool f32_in, hi
   return nw == 4 ? dq_one<64, 4>(a, f32_in, stream) : dq_one<64, 1>(a, f32_in, stream);
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs &a, int nw, int head_dim, bool f32_in, hipStream_t stream) {
+hipError_t launch_bwd_dkdv(const BwdArgs &a, int pairs, int head_dim, bool f32_in, hipStream_t stream) {
   if (a.n_blocks <= 0) return hipSuccess;
-  if (head_dim == 128) return nw == 4 ? dkdv_one<128, 4>(a, f32_in, stream) : dkdv_one<128, 1>(a, f32_in, stream);
-  return nw == 4 ? dkdv_one<64, 4>(a, f32_in, stream) : dkdv_one<64, 1>(a, f32_in, stream);
+  if (head_dim == 128) {
+    if (pairs == 6) return dkdv_one<128, 6>(a, f32_in, stream);
+    if (pairs == 4) return dkdv_one<128, 4>(a, f32_in, stream);
+    return dkdv_one<128, 1>(a, f32_in, stream);
+  }
+  if (pairs == 6) return dkdv_one<64, 6>(a, f32_in, stream);
+  if (pairs == 4) return dkdv_one<64, 4>(a, f32_in, stream);
+  return dkdv_one<64, 1>(a, f32_in, stream);
 }
 
 }  // namespace sta

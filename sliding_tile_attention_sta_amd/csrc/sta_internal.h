@@ -42,11 +42,11 @@ constexpr long long kMaxLds = 160 * 1024;
 // dK/dV) through LDS rings of two fp16 tensors with the forward's padded row
 // stride: two stages for dQ, three for dK/dV, which also keeps the blocks'
 // log-sum-exp and delta rows and two stages of the probability exchange
-// between its wave pairs (up to 4 pairs x 2 KiB).  Both keep the tile-local
+// between its wave pairs (up to 6 pairs x 2 KiB).  Both keep the tile-local
 // row offsets and the item's tile base rows.  The dK/dV layout is the larger.
 constexpr int bwd_stride(int head_dim) { return 2 * head_dim + 32; }
 constexpr long long bwd_lds_bytes(int head_dim, long long tile_tokens, long long max_list) {
-  return 3LL * 2 * kKeyBlock * bwd_stride(head_dim) + 3LL * 2 * kKeyBlock * 4 + 2LL * 4 * 2048 +
+  return 3LL * 2 * kKeyBlock * bwd_stride(head_dim) + 3LL * 2 * kKeyBlock * 4 + 2LL * 6 * 2048 +
          4LL * (tile_tokens + max_list);
 }
 
@@ -86,14 +86,15 @@ struct sta_plan {
   int32_t subs = 0;       // work items per (b, head, query tile)
 
   // Backward: inverse lists (query tiles whose window holds a key tile) and
-  // the schedules of the dQ and dK/dV kernels, whose items own
-  // 32 * bwd_nw tokens of one tile.
+  // the schedules of the dQ kernel (items of 32 * bwd_q_waves queries) and
+  // the dK/dV kernel (items of 32 * bwd_k_pairs keys).
   std::vector<int32_t> q_off;     // heads*n_tiles + 1
   std::vector<int32_t> q_idx;
   std::vector<int32_t> sched_dq, sched_dkdv;
   int32_t max_nq = 0;     // longest inverse list
-  int32_t bwd_nw = 0;     // waves per backward work item
-  int32_t bwd_subs = 0;   // backward work items per (b, head, tile)
+  int32_t bwd_q_waves = 0;   // waves per dQ work item
+  int32_t bwd_k_pairs = 0;   // wave pairs per dK/dV work item
+  int32_t bwd_q_subs = 0, bwd_k_subs = 0;   // work items per (b, head, tile)
   bool bwd_ok = false;    // the backward kernels' LDS fits
 
   mutable std::mutex mu;

@@ -49,9 +49,10 @@ struct BwdArgs {
 // delta[r] = sum_d dO[r, d] * O[r, d] for rows r < rows.
 hipError_t launch_bwd_delta(const void *o, const void *dout, float *delta, int64_t rows, int head_dim,
                             bool f32_o, bool f32_g, hipStream_t stream);
-// dQ and dK/dV kernels; nw = waves per work item (32 tokens per wave).
+// dQ kernel with nw waves of 32 queries per work item; dK/dV kernel with
+// `pairs` wave pairs of 32 keys per work item.
 hipError_t launch_bwd_dq(const BwdArgs &a, int nw, int head_dim, bool f32_in, hipStream_t stream);
-hipError_t launch_bwd_dkdv(const BwdArgs &a, int nw, int head_dim, bool f32_in, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs &a, int pairs, int head_dim, bool f32_in, hipStream_t stream);
 
 struct ReorderArgs {
   const void *in;

@@ -170,12 +170,18 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
         }
       }
     }
-    p->bwd_nw = p->V % 128 == 0 ? 4 : 1;
-    p->bwd_subs = p->V / (32 * p->bwd_nw);
+    p->bwd_q_waves = p->V % 128 == 0 ? 4 : 1;
+#ifndef STA_DKDV_PAIRS
+    p->bwd_k_pairs = p->V % 192 == 0 ? 6 : p->V % 128 == 0 ? 4 : 1;
+#else
+    p->bwd_k_pairs = p->V % (32 * STA_DKDV_PAIRS) == 0 ? STA_DKDV_PAIRS : 1;
+#endif
+    p->bwd_q_subs = p->V / (32 * p->bwd_q_waves);
+    p->bwd_k_subs = p->V / (32 * p->bwd_k_pairs);
     p->bwd_ok = bwd_lds_bytes(head_dim, p->V, std::max(p->max_nkv, p->max_nq)) <= kMaxLds;
     if (p->bwd_ok) {
-      p->sched_dq = build_schedule(p, p->kv_off, p->bwd_subs);
-      p->sched_dkdv = build_schedule(p, p->q_off, p->bwd_subs);
+      p->sched_dq = build_schedule(p, p->kv_off, p->bwd_q_subs);
+      p->sched_dkdv = build_schedule(p, p->q_off, p->bwd_k_subs);
     }
   } catch (const std::bad_alloc &) {
     delete p;
@@ -216,7 +222,8 @@ sta_status sta_plan_get_info(const sta_plan *p, sta_plan_info *info) {
   info->queries_per_item = p->qpi;
   info->kernel_variant = p->variant;
   info->bwd_supported = p->bwd_ok ? 1 : 0;
-  info->bwd_tokens_per_item = 32 * p->bwd_nw;
+  info->bwd_queries_per_item = 32 * p->bwd_q_waves;
+  info->bwd_keys_per_item = 32 * p->bwd_k_pairs;
   info->bwd_items_dq = (int64_t)p->sched_dq.size();
   info->bwd_items_dkdv = (int64_t)p->sched_dkdv.size();
   return STA_OK;

@@ -215,14 +215,15 @@ def test_backward_schedules_cover_every_item_once(name):
     p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
     info = p.info
     assert info.bwd_supported == 1
-    assert info.tile_tokens % info.bwd_tokens_per_item == 0
-    subs = info.tile_tokens // info.bwd_tokens_per_item
-    n_items = w.batch * w.heads * info.n_tiles * subs
-    for which, count in ((0, info.bwd_items_dq), (1, info.bwd_items_dkdv)):
+    for which, count, per in ((0, info.bwd_items_dq, info.bwd_queries_per_item),
+                              (1, info.bwd_items_dkdv, info.bwd_keys_per_item)):
+        assert info.tile_tokens % per == 0
+        n_items = w.batch * w.heads * info.n_tiles * (info.tile_tokens // per)
         s = p.schedule_bwd(which).numpy()
         assert len(s) == count and len(s) % 8 == 0
         assert sorted(s[s >= 0].tolist()) == list(range(n_items))
         assert (s[s < 0] == -1).all()
+    subs = info.tile_tokens // info.bwd_keys_per_item
     # the dK/dV items are ordered by the length of their inverse list
     s = p.schedule_bwd(1).numpy()
     for x in range(8):
