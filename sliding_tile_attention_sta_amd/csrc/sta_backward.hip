@@ -146,7 +146,10 @@ __device__ __forceinline__ Item decode(int item, const BwdArgs &a) {
 // dQ: queries resident, key blocks streamed.
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool F32IN>
-__global__ __launch_bounds__(NW * 64) void sta_bwd_dq_kernel(BwdArgs a) {
+// Two waves per SIMD: without the hint the allocator parks the Q and dO
+// fragments in AGPRs and copies them back every step (about 100 extra VALU
+// instructions per step).
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sta_bwd_dq_kernel(BwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QPI = 32 * NW;
   constexpr int STR = bwd_stride(D);
