@@ -15,7 +15,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_grad_out", "sample_query_tiles", "tile_count"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_grad_out", "make_local_qkv", "sample_query_tiles",
+           "tile_count"]
 
 
 @dataclass(frozen=True)
@@ -121,6 +122,46 @@ def make_grad_out(w: Workload, device: str | torch.device = "cpu"):
     x = torch.randn((w.batch, w.heads, T, H, W, w.head_dim), generator=g, device=dev,
                     dtype=torch.float32)
     return x.to(w.torch_dtype)
+
+
+def make_local_qkv(video, lengths, head_dim: int, batch: int = 1, sharpness: float = 8.0,
+                   noise: float = 0.1, seed: int = 0, dtype=torch.bfloat16,
+                   device: str | torch.device = "cpu"):
+    """Calibration inputs whose attention is local, one length scale per head.
+
+    The pages profile the locality of trained heads; with no trained model
+    here, head h gets queries and keys built from random Fourier features of
+    the token coordinates p = (t, y, z):
+        phi_h(p) = sqrt(2 / D) cos(W_h p + b_h),  W_h ~ N(0, I / l_h^2),
+        b_h ~ U(0, 2 pi),
+    q = sharpness * sqrt(D) * phi_h(p) + noise * N(0, 1),
+    k = phi_h(p) + noise * N(0, 1),  v ~ N(0, 1),
+    so that at scale 1/sqrt(D) a query's score for a key is about sharpness
+    times a Gaussian of their distance with width l_h tokens, and the head
+    attends to roughly its l_h-neighbourhood.  Shapes [B, heads, T, H, W, D]
+    in natural order; one generator seeded with ``seed`` on ``device``."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    T, H, W = video
+    heads = len(lengths)
+    t, y, z = torch.meshgrid(torch.arange(T, device=dev), torch.arange(H, device=dev),
+                             torch.arange(W, device=dev), indexing="ij")
+    pos = torch.stack([t, y, z], dim=-1).reshape(-1, 3).float()          # [N, 3]
+    qs, ks = [], []
+    for h in range(heads):
+        w = torch.randn((3, head_dim), generator=g, device=dev) / float(lengths[h])
+        b = torch.rand((head_dim,), generator=g, device=dev) * (2 * math.pi)
+        phi = math.sqrt(2.0 / head_dim) * torch.cos(pos @ w + b)          # [N, D]
+        qs.append(phi * (sharpness * math.sqrt(head_dim)))
+        ks.append(phi)
+    q = torch.stack(qs).unsqueeze(0).expand(batch, -1, -1, -1).clone()
+    k = torch.stack(ks).unsqueeze(0).expand(batch, -1, -1, -1).clone()
+    q += noise * torch.randn(q.shape, generator=g, device=dev)
+    k += noise * torch.randn(k.shape, generator=g, device=dev)
+    v = torch.randn(q.shape, generator=g, device=dev)
+    shape = (batch, heads, T, H, W, head_dim)
+    return tuple(x.reshape(shape).to(dtype) for x in (q, k, v))
 
 
 def sample_query_tiles(w: Workload, head: int, count: int = 64) -> list[tuple[int, int, int]]:

@@ -1,0 +1,187 @@
+"""Pins of the window-search oracle (oracle/sta_oracle_search.py), CPU only.
+
+  * a window covering the grid has error exactly zero,
+  * a constant V gives every window error zero, so the cheapest wins,
+  * attention confined to each query's own tile makes the 1x1x1 window
+    exact (closed form),
+  * the error of a candidate against torch's float64 dense attention,
+  * the choice satisfies its defining constraints on random error tables,
+  * planted mistakes in a copy of the oracle must each fail a pin.
+"""
+
+import math
+import types
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sta_oracle as F
+from oracle import sta_oracle_search as S
+
+VIDEO, TILE = (4, 6, 4), (2, 3, 2)
+GRID = (2, 2, 2)
+N, D = 96, 8
+
+
+def _rand(rng, heads=2):
+    return tuple(rng.standard_normal((1, heads, N, D)) for _ in range(3))
+
+
+def pin_full_window_is_exact(mod, seed=1):
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand(rng)
+    cands = [(2, 2, 2), (5, 9, 3), (1, 1, 1)]
+    err = mod.window_errors(q, k, v, VIDEO, TILE, cands, scale=0.4)
+    fails = []
+    if not (err[:, 0] == 0).all() or not (err[:, 1] == 0).all():
+        fails.append(("full window error", err[:, :2].tolist()))
+    if not (err[:, 2] > 0).all():
+        fails.append(("1x1x1 error not positive", err[:, 2].tolist()))
+    return fails
+
+
+def pin_constant_v(mod, seed=2):
+    rng = np.random.default_rng(seed)
+    q, k, _ = _rand(rng)
+    v = np.ones_like(q) * rng.standard_normal(D)
+    cands = S.odd_candidates(GRID) + [(1, 2, 1)]
+    err = mod.window_errors(q, k, v, VIDEO, TILE, cands, scale=0.4)
+    fails = []
+    if not np.allclose(err, 0.0, atol=1e-12):
+        fails.append(("constant v", float(np.abs(err).max())))
+    if mod.select_windows(err, cands, GRID, 1e-9) != [(1, 1, 1)] * 2:
+        fails.append(("constant v choice", mod.select_windows(err, cands, GRID, 1e-9)))
+    return fails
+
+
+def pin_tile_confined_attention(mod):
+    # q_x = alpha e_tile(x), k_y = e_tile(y): scores are alpha within the
+    # query's own tile and 0 elsewhere, so with alpha = 80 every other tile
+    # carries a relative weight below e^-80 and the 1x1x1 window is exact.
+    coords = F.natural_coords(VIDEO)
+    tid = [(c[0] // TILE[0]) * 4 + (c[1] // TILE[1]) * 2 + c[2] // TILE[2] for c in coords]
+    q = np.zeros((1, 1, N, D))
+    k = np.zeros((1, 1, N, D))
+    for n, t in enumerate(tid):
+        q[0, 0, n, t] = 80.0
+        k[0, 0, n, t] = 1.0
+    v = np.random.default_rng(3).standard_normal((1, 1, N, D))
+    cands = [(2, 2, 2), (1, 2, 1), (1, 1, 1), (2, 1, 2)]
+    err = mod.window_errors(q, k, v, VIDEO, TILE, cands, scale=1.0)
+    fails = []
+    if not err[0, 2] < 1e-30:
+        fails.append(("1x1x1 not exact", float(err[0, 2])))
+    if mod.select_windows(err, cands, GRID, 1e-20) != [(1, 1, 1)]:
+        fails.append(("choice", mod.select_windows(err, cands, GRID, 1e-20)))
+    return fails
+
+
+def pin_error_against_dense_library(mod, seed=4):
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand(rng)
+    scale = 1.0 / math.sqrt(D)
+    cands = [(1, 2, 1), (2, 1, 1)]
+    err = mod.window_errors(q, k, v, VIDEO, TILE, cands, scale=scale)
+    dense = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x) for x in (q, k, v)), scale=scale).numpy()
+    fails = []
+    for c, w in enumerate(cands):
+        o = F.sta_forward_explicit(q, k, v, VIDEO, TILE, [w] * 2, scale=scale)
+        for h in range(2):
+            want = np.linalg.norm(o[:, h] - dense[:, h]) / np.linalg.norm(dense[:, h])
+            if abs(err[h, c] - want) > 1e-12:
+                fails.append(("error", h, w, float(err[h, c]), float(want)))
+    return fails
+
+
+def pin_choice_constraints(mod, seed=5):
+    rng = np.random.default_rng(seed)
+    grid = (5, 6, 10)
+    cands = S.odd_candidates(grid) + [(7, 2, 3), (2, 2, 2), (3, 3, 3)]
+    fails = []
+    # a window wider than the grid costs its clamped extent: (7, 2, 3) costs
+    # 5 * 2 * 3 = 30 and beats (5, 1, 7) at 35
+    err = np.ones((1, len(cands)))
+    err[0, cands.index((7, 2, 3))] = 0.0
+    err[0, cands.index((5, 1, 7))] = 0.0
+    if mod.select_windows(err, cands, grid, 0.5) != [(7, 2, 3)]:
+        fails.append(("clamped cost", mod.select_windows(err, cands, grid, 0.5)))
+    # nothing meets the threshold: the full window
+    if mod.select_windows(np.ones((2, len(cands))), cands, grid, 0.5) != [grid] * 2:
+        fails.append(("fallback", mod.select_windows(np.ones((2, len(cands))), cands, grid, 0.5)))
+    for trial in range(50):
+        err = rng.uniform(0, 1, size=(3, len(cands)))
+        err[:, rng.integers(len(cands))] = 0.25          # an exact tie somewhere
+        tau = float(rng.uniform(0.05, 0.6))
+        got = mod.select_windows(err, cands, grid, tau)
+        for h in range(3):
+            ok = [c for c in range(len(cands)) if err[h, c] <= tau]
+            if not ok:
+                if got[h] != grid:
+                    fails.append(("fallback", trial, h, got[h]))
+                continue
+            cost = lambda c: int(np.prod([min(a, n) for a, n in zip(cands[c], grid)]))
+            cmin = min(cost(c) for c in ok)
+            cheapest = [c for c in ok if cost(c) == cmin]
+            emin = min(err[h, c] for c in cheapest)
+            first = min(c for c in cheapest if err[h, c] == emin)
+            if got[h] != tuple(cands[first]):
+                fails.append(("choice", trial, h, got[h], cands[first]))
+    return fails
+
+
+ALL_PINS = [pin_full_window_is_exact, pin_constant_v, pin_tile_confined_attention,
+            pin_error_against_dense_library, pin_choice_constraints]
+
+
+def run_pins(mod):
+    fails = []
+    for p in ALL_PINS:
+        try:
+            fails += [(p.__name__, f) for f in p(mod)]
+        except Exception as e:  # a mutant may also crash
+            fails.append((p.__name__, repr(e)))
+    return fails
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(pin):
+    assert pin(S) == []
+
+
+def test_odd_candidates():
+    assert S.odd_candidates((5, 6, 10))[:3] == [(1, 1, 1), (1, 1, 3), (1, 1, 5)]
+    assert len(S.odd_candidates((5, 6, 10))) == 3 * 4 * 6
+    assert S.odd_candidates((1, 2, 1)) == [(1, 1, 1), (1, 2, 1)]
+
+
+MUTANTS = [
+    ("normalised by the candidate", "den = math.sqrt(float((full[:, h] ** 2).sum()))",
+     "den = math.sqrt(float((o[:, h] ** 2).sum()))"),
+    ("squared error", "err[h, c] = num / den", "err[h, c] = (num / den) ** 2"),
+    ("cost without clamp", "we = F.effective_window(window, grid)", "we = tuple(window)"),
+    ("tie to the larger error", "key = (window_cost(w, grid), err[h, c], c)",
+     "key = (window_cost(w, grid), -err[h, c], c)"),
+    ("fallback to the last candidate", "out.append(best[1] if best is not None else tuple(int(n) for n in grid))",
+     "out.append(best[1] if best is not None else tuple(candidates[-1]))"),
+    ("strict threshold", "if not err[h, c] <= threshold:", "if not err[h, c] < threshold:"),
+    ("dense reference with a 3-tile window",
+     "full = F.sta_forward_explicit(q, k, v, video, tile, [grid] * heads, scale=scale)",
+     "full = F.sta_forward_explicit(q, k, v, video, tile, [(3, 3, 3)] * heads, scale=scale)"),
+]
+
+
+def _mutant(src, old, new, tag):
+    assert old in src, tag
+    mod = types.ModuleType("sta_oracle_search_mutant")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new, 1), f"<mutant {tag}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("tag,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tag, old, new):
+    with open(S.__file__) as f:
+        src = f.read()
+    assert run_pins(_mutant(src, old, new, tag)) != [], f"mutant '{tag}' survived every pin"
