@@ -107,6 +107,11 @@ def pin_choice_constraints(mod, seed=5):
     err[0, cands.index((5, 1, 7))] = 0.0
     if mod.select_windows(err, cands, grid, 0.5) != [(7, 2, 3)]:
         fails.append(("clamped cost", mod.select_windows(err, cands, grid, 0.5)))
+    # an error equal to the threshold is within it
+    err = np.ones((1, len(cands)))
+    err[0, 0] = 0.3
+    if mod.select_windows(err, cands, grid, 0.3) != [cands[0]]:
+        fails.append(("threshold inclusive", mod.select_windows(err, cands, grid, 0.3)))
     # nothing meets the threshold: the full window
     if mod.select_windows(np.ones((2, len(cands))), cands, grid, 0.5) != [grid] * 2:
         fails.append(("fallback", mod.select_windows(np.ones((2, len(cands))), cands, grid, 0.5)))
