@@ -78,16 +78,18 @@ def pin_tile_confined_attention(mod):
 
 
 def pin_error_against_dense_library(mod, seed=4):
+    # grid (6, 3, 2): a 3x3x3 window is not the whole grid here
+    video, tile = (6, 6, 4), (1, 2, 2)
     rng = np.random.default_rng(seed)
-    q, k, v = _rand(rng)
+    q, k, v = (rng.standard_normal((1, 2, 144, D)) for _ in range(3))
     scale = 1.0 / math.sqrt(D)
-    cands = [(1, 2, 1), (2, 1, 1)]
-    err = mod.window_errors(q, k, v, VIDEO, TILE, cands, scale=scale)
+    cands = [(1, 2, 1), (3, 3, 3), (5, 1, 2)]
+    err = mod.window_errors(q, k, v, video, tile, cands, scale=scale)
     dense = torch.nn.functional.scaled_dot_product_attention(
         *(torch.from_numpy(x) for x in (q, k, v)), scale=scale).numpy()
     fails = []
     for c, w in enumerate(cands):
-        o = F.sta_forward_explicit(q, k, v, VIDEO, TILE, [w] * 2, scale=scale)
+        o = F.sta_forward_explicit(q, k, v, video, tile, [w] * 2, scale=scale)
         for h in range(2):
             want = np.linalg.norm(o[:, h] - dense[:, h]) / np.linalg.norm(dense[:, h])
             if abs(err[h, c] - want) > 1e-12:
