@@ -35,8 +35,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
-                    help="forward (the metric line) or backward (delta + dQ + dK/dV kernels)")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "search"], default="forward",
+                    help="forward (the metric line), backward (delta + dQ + dK/dV kernels) or "
+                         "search (per-head window search over the default candidates)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -153,6 +154,53 @@ def backward(args, w, plan, q, k, v, stream):
     }
 
 
+def search(args, w, stream):
+    """One step = one sweep of the per-head window search over the default
+    candidates of the workload's grid, on a locality calibration input of
+    the workload's shape: head h has length scale l_h = 4 * 2^(h mod 6)
+    tokens, i.e. attends to a Gaussian neighbourhood about l_h / 4 = 1 to 32
+    tokens wide.  The sweep runs the forward once with
+    the full window and once per candidate, plus the error reduction, and
+    synchronises once per candidate."""
+    import torch
+    from sliding_tile_attention_sta_amd import api
+    from sliding_tile_attention_sta_amd.synthetic import make_local_qkv
+
+    lengths = [4.0 * 2 ** (h % 6) for h in range(w.heads)]
+    q, k, v = make_local_qkv(w.video, lengths, w.head_dim, batch=w.batch, sharpness=16.0,
+                             seed=w.seed + 900, dtype=torch.bfloat16, device="cuda:0")
+    grid = tuple(e // t for e, t in zip(w.video, w.tile))
+    cands = api.window_candidates(grid)
+    for _ in range(args.warmup):
+        api.window_errors(q, k, v, w.tile, cands[:2], stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        err = api.window_errors(q, k, v, w.tile, cands, stream=stream)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    V = w.tile[0] * w.tile[1] * w.tile[2]
+    n_tiles = grid[0] * grid[1] * grid[2]
+    per_pair = 4.0 * V * V * w.head_dim * w.heads * w.batch
+    pairs = n_tiles * (n_tiles + sum(min(a, grid[0]) * min(b, grid[1]) * min(c, grid[2]) for a, b, c in cands))
+    flops = per_pair * pairs
+    tau = 0.1
+    windows = api.window_select(err, cands, grid, tau)
+    kept = sum(a * b * c for a, b, c in windows) / (len(windows) * n_tiles)
+    return {
+        "metric": "STA per-head window search: seconds per candidate sweep",
+        "value": round(sec, 3), "unit": "s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 1), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (locality calibration inputs)",
+        "config": {"workload": w.name + "-locality", "video": list(w.video), "tile": list(w.tile),
+                   "heads": w.heads, "head_dim": w.head_dim, "lengths": lengths,
+                   "candidates": len(cands), "threshold": tau},
+        "forward_tflops": round(flops / sec / 1e12, 1),
+        "chosen_windows": windows,
+        "attended_fraction_of_dense": round(kept, 4),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -183,6 +231,10 @@ def main():
     plan = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
     if args.which == "backward":
         print(json.dumps(backward(args, w, plan, q, k, v, stream)), flush=True)
+        return
+    if args.which == "search":
+        del q, k, v
+        print(json.dumps(search(args, w, stream)), flush=True)
         return
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     flops = plan.flops

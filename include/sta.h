@@ -202,6 +202,45 @@ sta_status sta_forward(const void *q, const void *k, const void *v, void *out, i
                        float scale, sta_dtype in_dtype, sta_dtype out_dtype, sta_layout layout,
                        void *stream);
 
+/* ---- Per-head window search -------------------------------------------
+ * The pages configure each head's window automatically from the profiled
+ * locality of its attention (index page, Abstract; gptget summary page,
+ * Methodology, Technical Contribution and Limitations), giving no formula.
+ * Reading implemented here: on calibration inputs, the error of candidate
+ * window c for head h is ||O_c - O_full|| / ||O_full|| (Frobenius norm over
+ * the batch, tokens and channels of head h, O_full = attention over the
+ * whole video); each head gets the cheapest candidate, cost =
+ * prod(min(w, grid)) key tiles per query tile, whose error is at most a
+ * threshold (ties: smaller error, then earlier candidate), else the full
+ * window (the grid). */
+
+/* err[h * n_cand + c] for the candidate windows candidates[3c .. 3c+2] (in
+ * tiles) on one calibration input q, k, v ([batch, heads, N, head_dim] of
+ * in_dtype, DEVICE pointers, token order of layout).  err: HOST buffer of
+ * heads * n_cand doubles.  Runs the forward once with the full window and
+ * once per candidate (all heads at once) on stream, with fp32 outputs; the
+ * library allocates two fp32 [batch, heads, N, head_dim] device buffers for
+ * the call and frees them, and the call synchronises stream.
+ * Errors: as sta_plan_create and sta_forward_plan; STA_ERR_ALLOC. */
+sta_status sta_window_errors(const void *q, const void *k, const void *v, int batch, int heads, int T,
+                             int H, int W, const int tile[3], int head_dim, float scale,
+                             sta_dtype in_dtype, sta_layout layout, const int *candidates,
+                             int n_cand, double *err, void *stream);
+
+/* Host only.  window_out[3h .. 3h+2] = the window chosen for head h from
+ * err (heads x n_cand, e.g. sta_window_errors averaged over several
+ * calibration inputs) under threshold, by the rule above.  grid: tiles on
+ * (T, H, W).  STA_ERR_ARG on NULL or non-positive sizes. */
+sta_status sta_window_select(int heads, const int grid[3], const int *candidates, int n_cand,
+                             const double *err, double threshold, int *window_out);
+
+/* Host only.  The default candidate set for a grid: on each axis every odd
+ * extent below the axis length, and the axis length itself; all
+ * combinations in raster order, written as triples to out (cap triples).
+ * *count receives the number of candidates even when it exceeds cap (then
+ * STA_ERR_ARG). */
+sta_status sta_window_candidates(const int grid[3], int *out, int cap, int *count);
+
 /* Destroy every cached plan.  Not safe while another thread is in sta_forward. */
 sta_status sta_clear_plan_cache(void);
 

@@ -55,6 +55,10 @@ SIGNATURES = {
                                _I, _P]),
     "sta_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _IP, _IP, _I, ctypes.c_float,
                          _I, _I, _I, _P]),
+    "sta_window_errors": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _IP, _I, ctypes.c_float, _I, _I, _IP, _I,
+                               ctypes.POINTER(ctypes.c_double), _P]),
+    "sta_window_select": (_I, [_I, _IP, _IP, _I, ctypes.POINTER(ctypes.c_double), ctypes.c_double, _IP]),
+    "sta_window_candidates": (_I, [_IP, _IP, _I, _IP]),
     "sta_clear_plan_cache": (_I, []),
     "sta_status_string": (ctypes.c_char_p, [_I]),
 }

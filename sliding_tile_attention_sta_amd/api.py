@@ -18,6 +18,7 @@ from . import _lib as L
 __all__ = [
     "Plan", "sta_plan_create", "sta_tile_reorder", "sta_tile_unreorder", "sta_forward_plan",
     "sta_backward_plan", "sta_attention", "sta_forward", "sta_clear_plan_cache", "StaError",
+    "window_candidates", "window_errors", "window_select", "window_search",
 ]
 
 StaError = L.StaError
@@ -284,6 +285,80 @@ def sta_forward(q, k, v, tile, windows, scale: float | None = None, out=None,
                              _DTYPES[q.dtype], _DTYPES[out.dtype], _LAYOUTS[layout], _stream(stream))
     L.check(st, "sta_forward")
     return out
+
+
+def window_candidates(grid) -> list[tuple[int, int, int]]:
+    """The library's default candidate windows for a tile grid."""
+    g = _ints(grid)
+    cnt = ctypes.c_int()
+    L.lib().sta_window_candidates(g, None, 0, ctypes.byref(cnt))
+    buf = (ctypes.c_int * (3 * max(1, cnt.value)))()
+    L.check(L.lib().sta_window_candidates(g, buf, cnt.value, ctypes.byref(cnt)), "sta_window_candidates")
+    return [tuple(buf[3 * i:3 * i + 3]) for i in range(cnt.value)]
+
+
+def window_errors(q, k, v, tile, candidates, scale: float | None = None, layout: str = "natural",
+                  video=None, stream=None):
+    """[heads, n_cand] relative errors of STA against full attention for
+    each candidate window, on one calibration input (natural
+    [B, heads, T, H, W, D], or [B, heads, N, D] with video=(T, H, W))."""
+    import numpy as np
+    if q.dim() == 6:
+        B, heads, T, H, W, D = q.shape
+    else:
+        if video is None:
+            raise ValueError("video=(T, H, W) is required for 4-D inputs")
+        B, heads, _, D = q.shape
+        T, H, W = video
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if not x.is_cuda or not x.is_contiguous() or x.dtype not in _DTYPES or x.shape != q.shape \
+                or x.dtype != q.dtype:
+            raise ValueError(f"{name}: contiguous CUDA bf16/fp32 tensor shaped like q required")
+    cands = [int(x) for w in candidates for x in w]
+    n = len(cands) // 3
+    err = (ctypes.c_double * (heads * n))()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = L.lib().sta_window_errors(_ptr(q), _ptr(k), _ptr(v), int(B), int(heads), int(T), int(H), int(W),
+                                   _ints(tile), int(D), float(scale), _DTYPES[q.dtype], _LAYOUTS[layout],
+                                   _ints(cands), n, err, _stream(stream))
+    L.check(st, "sta_window_errors")
+    return np.array(err[:], dtype=np.float64).reshape(heads, n)
+
+
+def window_select(err, candidates, grid, threshold: float) -> list[tuple[int, int, int]]:
+    """Per head, the cheapest candidate within threshold (else the grid)."""
+    import numpy as np
+    err = np.ascontiguousarray(err, dtype=np.float64)
+    heads, n = err.shape
+    cands = [int(x) for w in candidates for x in w]
+    if len(cands) != 3 * n:
+        raise ValueError("one error column per candidate")
+    out = (ctypes.c_int * (3 * heads))()
+    st = L.lib().sta_window_select(heads, _ints(grid), _ints(cands), n,
+                                   err.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), float(threshold),
+                                   out)
+    L.check(st, "sta_window_select")
+    return [tuple(out[3 * h:3 * h + 3]) for h in range(heads)]
+
+
+def window_search(samples, tile, threshold: float, candidates=None, scale: float | None = None,
+                  layout: str = "natural", stream=None):
+    """Per-head windows from calibration inputs: ``samples`` is an iterable
+    of (q, k, v) in natural [B, heads, T, H, W, D] order.  The errors are
+    averaged over the samples before the choice.  Returns (windows, mean
+    errors, candidates)."""
+    errs, video = [], None
+    for q, k, v in samples:
+        video = tuple(q.shape[2:5])
+        grid = tuple(e // t for e, t in zip(video, tile))
+        cands = candidates if candidates is not None else window_candidates(grid)
+        errs.append(window_errors(q, k, v, tile, cands, scale=scale, layout=layout, stream=stream))
+    if not errs:
+        raise ValueError("no calibration samples")
+    mean = sum(errs) / len(errs)
+    grid = tuple(e // t for e, t in zip(video, tile))
+    return window_select(mean, cands, grid, threshold), mean, cands
 
 
 def sta_clear_plan_cache() -> None:

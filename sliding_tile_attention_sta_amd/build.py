@@ -24,7 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsta.so")
 
-HIP_SOURCES = ["sta_api.hip", "sta_forward.hip", "sta_backward.hip", "sta_reorder.hip"]
+HIP_SOURCES = ["sta_api.hip", "sta_forward.hip", "sta_backward.hip", "sta_reorder.hip", "sta_search.hip"]
 # Per-file extra flags.  The forward kernel needs no IEEE signalling-NaN
 # quieting, which lets v_max_f32 read MFMA results without canonicalising them.
 HIP_EXTRA = {"sta_forward.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}

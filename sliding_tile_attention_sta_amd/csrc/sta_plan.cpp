@@ -279,6 +279,53 @@ sta_status sta_plan_schedule(const sta_plan *p, int32_t *out, int64_t cap, int64
   return STA_OK;
 }
 
+sta_status sta_window_candidates(const int grid[3], int *out, int cap, int *count) {
+  if (!grid || !count) return STA_ERR_ARG;
+  for (int d = 0; d < 3; ++d)
+    if (grid[d] < 1) return STA_ERR_ARG;
+  std::vector<int> axis[3];
+  for (int d = 0; d < 3; ++d) {
+    for (int w = 1; w < grid[d]; w += 2) axis[d].push_back(w);
+    axis[d].push_back(grid[d]);
+  }
+  const int n = (int)(axis[0].size() * axis[1].size() * axis[2].size());
+  *count = n;
+  if (cap < n || !out) return STA_ERR_ARG;
+  int i = 0;
+  for (int a : axis[0])
+    for (int b : axis[1])
+      for (int c : axis[2]) {
+        out[3 * i] = a; out[3 * i + 1] = b; out[3 * i + 2] = c;
+        ++i;
+      }
+  return STA_OK;
+}
+
+sta_status sta_window_select(int heads, const int grid[3], const int *candidates, int n_cand,
+                             const double *err, double threshold, int *window_out) {
+  if (heads < 1 || !grid || !candidates || n_cand < 1 || !err || !window_out) return STA_ERR_ARG;
+  for (int d = 0; d < 3; ++d)
+    if (grid[d] < 1) return STA_ERR_ARG;
+  for (int i = 0; i < 3 * n_cand; ++i)
+    if (candidates[i] < 1) return STA_ERR_ARG;
+  for (int h = 0; h < heads; ++h) {
+    int best = -1;
+    long long best_cost = 0;
+    double best_err = 0.0;
+    for (int c = 0; c < n_cand; ++c) {
+      const double e = err[(size_t)h * n_cand + c];
+      if (!(e <= threshold)) continue;
+      long long cost = 1;
+      for (int d = 0; d < 3; ++d) cost *= std::min(candidates[3 * c + d], grid[d]);
+      if (best < 0 || cost < best_cost || (cost == best_cost && e < best_err)) {
+        best = c; best_cost = cost; best_err = e;
+      }
+    }
+    for (int d = 0; d < 3; ++d) window_out[3 * h + d] = best < 0 ? grid[d] : candidates[3 * best + d];
+  }
+  return STA_OK;
+}
+
 const char *sta_status_string(sta_status s) {
   switch (s) {
     case STA_OK: return "STA_OK";

@@ -1,0 +1,159 @@
+// Per-head window search for Sliding Tile Attention.
+//
+// The pages configure each head's window automatically from the profiled
+// locality of its attention ("Fast Video Generation with Sliding Tile
+// Attention", arXiv 2502.04507: index page, Abstract; gptget summary page,
+// Methodology, Technical Contribution, Novelty and Limitations) without a
+// formula.  Reading used here: on calibration inputs, the error of a
+// candidate window for head h is ||O_c - O_full|| / ||O_full|| over the
+// head's outputs; each head takes the cheapest candidate (fewest key tiles
+// per query tile) whose error is within a threshold, else the full window.
+//
+// The outputs come from the forward kernel (one call per candidate, every
+// head at once); the norms from a reduction kernel below, which reads the
+// two fp32 outputs once (HBM bound) and writes per-block partial sums that
+// the host adds in a fixed order, so the errors are deterministic.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "sta_internal.h"
+#include "sta_launch.h"
+
+namespace sta {
+namespace {
+
+constexpr int kRedThreads = 256;
+constexpr int kRedBlocksPerPlane = 64;
+
+// part[(plane * kRedBlocksPerPlane + blk) * 2 + {0, 1}] =
+//   (sum (a - b)^2, sum b^2) over the block's share of one [N, D] plane.
+__global__ __launch_bounds__(kRedThreads) void sq_diff_kernel(const float *a, const float *b,
+                                                              double *part, int64_t plane_elems) {
+  const int64_t plane = blockIdx.y;
+  const float4 *pa = reinterpret_cast<const float4 *>(a + plane * plane_elems);
+  const float4 *pb = reinterpret_cast<const float4 *>(b + plane * plane_elems);
+  const int64_t n4 = plane_elems / 4;
+  double sd = 0.0, sr = 0.0;
+  for (int64_t i = (int64_t)blockIdx.x * kRedThreads + threadIdx.x; i < n4;
+       i += (int64_t)kRedBlocksPerPlane * kRedThreads) {
+    const float4 x = pa[i], y = pb[i];
+    const float d0 = x.x - y.x, d1 = x.y - y.y, d2 = x.z - y.z, d3 = x.w - y.w;
+    sd += (double)(d0 * d0 + d1 * d1) + (double)(d2 * d2 + d3 * d3);
+    sr += (double)(y.x * y.x + y.y * y.y) + (double)(y.z * y.z + y.w * y.w);
+  }
+  __shared__ double red[2][kRedThreads];
+  red[0][threadIdx.x] = sd;
+  red[1][threadIdx.x] = sr;
+  __syncthreads();
+  for (int s = kRedThreads / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + s];
+      red[1][threadIdx.x] += red[1][threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double *o = part + (plane * kRedBlocksPerPlane + blockIdx.x) * 2;
+    o[0] = red[0][0];
+    o[1] = red[1][0];
+  }
+}
+
+struct DevBuf {
+  void *p = nullptr;
+  ~DevBuf() {
+    if (p) (void)hipFree(p);
+  }
+};
+
+struct PlanHolder {
+  sta_plan *p = nullptr;
+  ~PlanHolder() {
+    if (p) sta_plan_destroy(p);
+  }
+};
+
+}  // namespace
+}  // namespace sta
+
+extern "C" {
+
+sta_status sta_window_errors(const void *q, const void *k, const void *v, int batch, int heads, int T,
+                             int H, int W, const int tile[3], int head_dim, float scale,
+                             sta_dtype in_dtype, sta_layout layout, const int *candidates,
+                             int n_cand, double *err, void *stream) {
+  if (!q || !k || !v || !tile || !candidates || !err || n_cand < 1 || heads < 1 || batch < 1)
+    return STA_ERR_ARG;
+  for (int i = 0; i < 3 * n_cand; ++i)
+    if (candidates[i] < 1) return STA_ERR_ARG;
+  for (int d = 0; d < 3; ++d)
+    if (tile[d] < 1) return STA_ERR_ARG;
+  const int ext[3] = {T, H, W};
+  for (int d = 0; d < 3; ++d)
+    if (ext[d] < 1) return STA_ERR_ARG;
+  for (int d = 0; d < 3; ++d)
+    if (ext[d] % tile[d] != 0) return STA_ERR_SHAPE;
+  const int grid[3] = {T / tile[0], H / tile[1], W / tile[2]};
+
+  // Full-attention plan (window = grid for every head) and its output.
+  std::vector<int> win((size_t)heads * 3);
+  for (int h = 0; h < heads; ++h)
+    for (int d = 0; d < 3; ++d) win[h * 3 + d] = grid[d];
+  sta::PlanHolder full;
+  sta_status st = sta_plan_create(batch, heads, T, H, W, tile, win.data(), head_dim, &full.p);
+  if (st != STA_OK) return st;
+  const int64_t plane = (int64_t)T * H * W * head_dim;
+  const size_t out_bytes = (size_t)batch * heads * plane * sizeof(float);
+  const size_t part_count = (size_t)batch * heads * sta::kRedBlocksPerPlane * 2;
+  sta::DevBuf ref, cand, part;
+  if (hipMalloc(&ref.p, out_bytes) != hipSuccess || hipMalloc(&cand.p, out_bytes) != hipSuccess ||
+      hipMalloc(&part.p, part_count * sizeof(double)) != hipSuccess)
+    return STA_ERR_ALLOC;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Once work is queued, every exit drains the stream before the plans and
+  // buffers it uses are released.
+  auto fail = [&](sta_status e) {
+    (void)hipStreamSynchronize(s);
+    return e;
+  };
+  st = sta_forward_plan(full.p, q, k, v, ref.p, scale, in_dtype, STA_F32, layout, stream);
+  if (st != STA_OK) return fail(st);
+
+  std::vector<double> host(part_count);
+  for (int c = 0; c < n_cand; ++c) {
+    for (int h = 0; h < heads; ++h)
+      for (int d = 0; d < 3; ++d) win[h * 3 + d] = candidates[c * 3 + d];
+    sta::PlanHolder cp;
+    st = sta_plan_create(batch, heads, T, H, W, tile, win.data(), head_dim, &cp.p);
+    if (st != STA_OK) return fail(st);
+    st = sta_forward_plan(cp.p, q, k, v, cand.p, scale, in_dtype, STA_F32, layout, stream);
+    if (st != STA_OK) return fail(st);
+    hipLaunchKernelGGL(sta::sq_diff_kernel, dim3(sta::kRedBlocksPerPlane, batch * heads),
+                       dim3(sta::kRedThreads), 0, s, static_cast<const float *>(cand.p),
+                       static_cast<const float *>(ref.p), static_cast<double *>(part.p), plane);
+    if (hipGetLastError() != hipSuccess) return fail(STA_ERR_HIP);
+    if (hipMemcpyAsync(host.data(), part.p, part_count * sizeof(double), hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return fail(STA_ERR_HIP);
+    // The plan's device tables were used by the launch above; the stream
+    // has drained, so the plan may go.
+    for (int h = 0; h < heads; ++h) {
+      double sd = 0.0, sr = 0.0;
+      for (int b = 0; b < batch; ++b)
+        for (int i = 0; i < sta::kRedBlocksPerPlane; ++i) {
+          const double *x = &host[(((size_t)b * heads + h) * sta::kRedBlocksPerPlane + i) * 2];
+          sd += x[0];
+          sr += x[1];
+        }
+      err[(size_t)h * n_cand + c] = sr > 0.0 ? std::sqrt(sd) / std::sqrt(sr) : (sd > 0.0 ? INFINITY : 0.0);
+    }
+  }
+  return STA_OK;
+}
+
+}  // extern "C"

@@ -268,3 +268,44 @@ def test_backward_argument_errors_precede_device_work():
     assert lib.sta_forward_plan_lse(p.handle, q, k, v, o, None, 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
     assert lib.sta_forward_plan_lse(p.handle, q, k, v, o, P((3 << 40) + 8), 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
     assert lib.sta_forward_plan_lse(None, q, k, v, o, lse, 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
+
+
+# ---------------------------------------------------------------------------
+# Window search (host parts)
+# ---------------------------------------------------------------------------
+
+def test_window_candidates_match_oracle():
+    from oracle import sta_oracle_search as OS
+    for grid in [(5, 6, 10), (1, 1, 1), (3, 4, 4), (2, 7, 1)]:
+        assert api.window_candidates(grid) == OS.odd_candidates(grid)
+
+
+def test_window_select_matches_oracle():
+    import numpy as np
+    from oracle import sta_oracle_search as OS
+    rng = np.random.default_rng(8)
+    for grid in [(5, 6, 10), (3, 4, 4)]:
+        cands = OS.odd_candidates(grid) + [(9, 1, 2), (2, 2, 2)]
+        for _ in range(40):
+            err = rng.uniform(0, 1, size=(5, len(cands)))
+            err[:, rng.integers(len(cands))] = 0.3
+            err[rng.integers(5)] = 2.0                     # a head with no candidate in range
+            for tau in (0.05, 0.3, 0.7):
+                assert api.window_select(err, cands, grid, tau) == OS.select_windows(err, cands, grid, tau)
+
+
+def test_window_search_argument_errors():
+    lib = L.lib()
+    P = ctypes.c_void_p
+    err = (ctypes.c_double * 4)()
+    t = _ints([2, 4, 4])
+    c = _ints([1, 1, 1, 3, 3, 3])
+    assert lib.sta_window_errors(None, P(1), P(2), 1, 2, 6, 16, 16, t, 64, 0.125, 0, 0, c, 2, err, None) == L.STA_ERR_ARG
+    assert lib.sta_window_errors(P(1), P(2), P(3), 1, 2, 7, 16, 16, t, 64, 0.125, 0, 0, c, 2, err, None) == L.STA_ERR_SHAPE
+    assert lib.sta_window_errors(P(1), P(2), P(3), 1, 2, 6, 16, 16, t, 64, 0.125, 0, 0, _ints([1, 0, 1]), 1, err, None) == L.STA_ERR_ARG
+    assert lib.sta_window_errors(P(1), P(2), P(3), 1, 2, 6, 16, 16, t, 80, 0.125, 0, 0, c, 2, err, None) == L.STA_ERR_UNSUPPORTED
+    out = _ints([0] * 6)
+    assert lib.sta_window_select(2, _ints([3, 4, 4]), c, 2, None, 0.1, out) == L.STA_ERR_ARG
+    assert lib.sta_window_select(0, _ints([3, 4, 4]), c, 2, err, 0.1, out) == L.STA_ERR_ARG
+    cnt = ctypes.c_int()
+    assert lib.sta_window_candidates(_ints([0, 1, 1]), None, 0, ctypes.byref(cnt)) == L.STA_ERR_ARG
