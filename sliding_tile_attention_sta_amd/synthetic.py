@@ -77,6 +77,14 @@ WORKLOADS = {
                      magnitude=(0.5, 4.0),
                      description="60x48x80 latent (230400 tokens), tile 6x8x8, window 3x3x3, "
                                  "24 heads, d128, bf16, per-token magnitude U(0.5, 4)"),
+    # 2D STA (an image latent: T = 1, tiles of one frame)
+    "2d": Workload("2d", 6, (1, 96, 96), (1, 16, 24), ((1, 3, 3),) * 8, 128, "bf16",
+                   description="2D: 96x96 latent, tile 16x24 (384 tokens), window 3x3 tiles, "
+                               "8 heads, d128, bf16"),
+    "2d-fine": Workload("2d-fine", 7, (1, 128, 128), (1, 8, 8),
+                        ((1, 5, 5), (1, 3, 3), (1, 9, 9), (1, 1, 1)), 64, "bf16",
+                        description="2D: 128x128 latent, tile 8x8, windows 5x5, 3x3, 9x9, 1x1 "
+                                    "tiles, 4 heads, d64, bf16"),
 }
 
 

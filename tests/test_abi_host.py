@@ -49,7 +49,7 @@ def test_status_strings():
     assert "unknown" in L.status_string(42)
 
 
-@pytest.mark.parametrize("name", ["tiny", "small", "720p", "mixed", "long"])
+@pytest.mark.parametrize("name", ["tiny", "small", "720p", "mixed", "long", "2d", "2d-fine"])
 def test_plan_matches_oracle_geometry(name):
     w = WORKLOADS[name]
     p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
@@ -194,7 +194,7 @@ def test_forward_argument_errors_precede_device_work():
 # Backward plan tables
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny", "small", "720p", "mixed"])
+@pytest.mark.parametrize("name", ["tiny", "small", "720p", "mixed", "2d", "2d-fine"])
 def test_inverse_lists_match_oracle(name):
     from oracle import sta_oracle_bwd as OB
     w = WORKLOADS[name]
