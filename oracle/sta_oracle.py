@@ -36,6 +36,11 @@ design notes of the repository):
   R4  scale defaults to 1/sqrt(head_dim).
   R5  Inputs are taken exactly as given (for bf16 workloads: the bf16 values,
       widened); all arithmetic here is float64.
+  R7  (Only when asked for, ``partial=True``.)  An extent that is not a
+      multiple of its tile size gets ceil(extent / tile) tiles; the last tile
+      on that axis is partial.  Tile coordinates, windows and the tile-level
+      mask are unchanged; only tokens that exist take part.  This equals
+      padding the video to whole tiles and masking the padded keys.
 
 Parity pins: every function below is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` (brute force, dense / block-diagonal special
@@ -70,16 +75,18 @@ __all__ = [
 # non-overlapping tiles and attention is done in local windows at tile level).
 # ---------------------------------------------------------------------------
 
-def tile_grid(video: Sequence[int], tile: Sequence[int]) -> tuple[int, int, int]:
+def tile_grid(video: Sequence[int], tile: Sequence[int], partial: bool = False) -> tuple[int, int, int]:
     """Number of tiles along (T, H, W).  Tiles do not overlap and cover the
-    video, so every extent must be a multiple of its tile size."""
+    video, so every extent must be a multiple of its tile size -- unless
+    partial is set (reading R7): then an axis has ceil(extent / tile) tiles
+    and its last tile holds only the tokens that exist."""
     if len(video) != 3 or len(tile) != 3:
         raise ValueError("video and tile must have three axes (T, H, W)")
     out = []
     for e, t in zip(video, tile):
-        if t <= 0 or e <= 0 or e % t != 0:
+        if t <= 0 or e <= 0 or (e % t != 0 and not partial):
             raise ValueError(f"extent {e} is not a positive multiple of tile {t}")
-        out.append(e // t)
+        out.append(-(-e // t))
     return tuple(out)
 
 
@@ -175,7 +182,7 @@ def _as_windows(windows, heads: int) -> list[tuple[int, int, int]]:
 def sta_forward_explicit(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                          video: Sequence[int], tile: Sequence[int], windows,
                          scale: float | None = None,
-                         coords: np.ndarray | None = None) -> np.ndarray:
+                         coords: np.ndarray | None = None, partial: bool = False) -> np.ndarray:
     """STA forward by the explicit N x N mask (small inputs only).
 
     q, k, v: [B, heads, N, D]; token n sits at coords[n] = (t, y, z)
@@ -184,7 +191,7 @@ def sta_forward_explicit(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     Returns float64 [B, heads, N, D].
     """
     B, heads, N, D = q.shape
-    grid = tile_grid(video, tile)
+    grid = tile_grid(video, tile, partial)
     if coords is None:
         coords = natural_coords(video)
     if coords.shape[0] != N:
@@ -210,7 +217,8 @@ def window_tiles(c: Sequence[int], window: Sequence[int], grid: Sequence[int]):
 def sta_forward_query_tiles(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                             tile: Sequence[int], window: Sequence[int], head: int,
                             query_tiles: Iterable[Sequence[int]],
-                            scale: float | None = None, batch: int = 0) -> list[np.ndarray]:
+                            scale: float | None = None, batch: int = 0,
+                            partial: bool = False) -> list[np.ndarray]:
     """STA forward for selected query tiles of one head (large inputs).
 
     q, k, v are in natural layout [B, heads, T, H, W, D] (any float dtype,
@@ -218,10 +226,11 @@ def sta_forward_query_tiles(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     the tokens of the window's key tiles -- which, because the window is a
     box of tiles on each axis, is the box of tokens
     [s_t*tT, (s_t+w_t)*tT) x [s_y*tH, ...) x [s_z*tW, ...).
-    Returns, per query tile, float64 [tT, tH, tW, D] in natural order.
+    Returns, per query tile, float64 [tT, tH, tW, D] in natural order
+    (smaller for a partial tile, reading R7: slices stop at the video's end).
     """
     _, _, T, H, W, D = q.shape
-    grid = tile_grid((T, H, W), tile)
+    grid = tile_grid((T, H, W), tile, partial)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     tT, tH, tW = tile
@@ -236,7 +245,8 @@ def sta_forward_query_tiles(q: np.ndarray, k: np.ndarray, v: np.ndarray,
         mask = np.ones((qt.shape[0], kt.shape[0]), dtype=bool)
         o = masked_softmax_attention(np.asarray(qt, np.float64), np.asarray(kt, np.float64),
                                      np.asarray(vt, np.float64), mask, scale)
-        outs.append(o.reshape(tT, tH, tW, -1))
+        outs.append(o.reshape(*q[batch, head, c[0] * tT:(c[0] + 1) * tT, c[1] * tH:(c[1] + 1) * tH,
+                                  c[2] * tW:(c[2] + 1) * tW].shape[:3], -1))
     return outs
 
 

@@ -434,3 +434,84 @@ def test_token_predicate_matches_bruteforce():
             want = set(bf_keys(tuple(coords[n]), video, tile, windows[0]))
             got = {j for j in range(len(coords)) if O.permitted(coords[n], coords[j], tile, windows[0], grid)}
             assert got == want
+
+
+# ---------------------------------------------------------------------------
+# Partial tiles (reading R7: extents that are not multiples of the tile)
+# ---------------------------------------------------------------------------
+
+def bf_keys_partial(qx, video, tile, window):
+    """Brute force with ceil(extent / tile) tiles: the window found by search
+    on that grid, then every EXISTING token of its tiles by nested loops."""
+    T, H, W = video
+    grid = [-(-video[i] // tile[i]) for i in range(3)]
+    c = [qx[i] // tile[i] for i in range(3)]
+    starts = [bf_start(c[i], window[i], grid[i]) for i in range(3)]
+    ext = [min(window[i], grid[i]) for i in range(3)]
+    keys = []
+    for a in range(starts[0], starts[0] + ext[0]):
+        for b in range(starts[1], starts[1] + ext[1]):
+            for cc in range(starts[2], starts[2] + ext[2]):
+                for lt in range(tile[0]):
+                    for ly in range(tile[1]):
+                        for lz in range(tile[2]):
+                            t, y, z = a * tile[0] + lt, b * tile[1] + ly, cc * tile[2] + lz
+                            if t < T and y < H and z < W:
+                                keys.append((t * H + y) * W + z)
+    return sorted(keys)
+
+
+def test_partial_tiles_against_bruteforce():
+    rng = np.random.default_rng(31)
+    done = 0
+    while done < 6:
+        tile = tuple(int(x) for x in rng.integers(2, 4, size=3))
+        video = tuple(int(x) for x in rng.integers(2, 9, size=3))
+        if all(v % t == 0 for v, t in zip(video, tile)) or np.prod(video) > 180:
+            continue
+        done += 1
+        windows = [tuple(int(x) for x in rng.integers(1, 5, size=3)) for _ in range(2)]
+        with pytest.raises(ValueError):
+            O.tile_grid(video, tile)
+        grid = O.tile_grid(video, tile, partial=True)
+        N, D = int(np.prod(video)), 3
+        coords = O.natural_coords(video)
+        q, k, v = (rng.standard_normal((1, 2, N, D)) for _ in range(3))
+        for h in range(2):
+            mask = O.sta_mask(coords, coords, tile, windows[h], grid)
+            for n in range(N):
+                assert np.flatnonzero(mask[n]).tolist() == bf_keys_partial(tuple(coords[n]), video, tile,
+                                                                           windows[h])
+        got = O.sta_forward_explicit(q, k, v, video, tile, windows, scale=0.6, partial=True)
+        T, H, W = video
+        for h in range(2):
+            for n in range(0, N, 5):
+                keys = bf_keys_partial(tuple(coords[n]), video, tile, windows[h])
+                s = 0.6 * (k[0, h, keys] @ q[0, h, n])
+                p = np.exp(s - s.max())
+                assert np.allclose(got[0, h, n], (p @ v[0, h, keys]) / p.sum(), rtol=0, atol=1e-12)
+            # per-query-tile function, partial tiles included
+            tiles = list(itertools.product(range(grid[0]), range(grid[1]), range(grid[2])))
+            outs = O.sta_forward_query_tiles(*(x.reshape(1, 2, T, H, W, D) for x in (q, k, v)), tile,
+                                             windows[h], h, tiles, scale=0.6, partial=True)
+            full = np.zeros((T, H, W, D))
+            for c, o in zip(tiles, outs):
+                full[c[0] * tile[0]:(c[0] + 1) * tile[0], c[1] * tile[1]:(c[1] + 1) * tile[1],
+                     c[2] * tile[2]:(c[2] + 1) * tile[2]] = o
+            assert np.allclose(full.reshape(N, D), got[0, h], rtol=0, atol=1e-12)
+
+
+def test_partial_tiles_dense_and_blockdiag():
+    rng = np.random.default_rng(32)
+    video, tile = (5, 7, 4), (2, 3, 3)
+    N, D = 140, 6
+    q, k, v = (rng.standard_normal((1, 2, N, D)) for _ in range(3))
+    got = O.sta_forward_explicit(q, k, v, video, tile, [(3, 3, 2), (9, 9, 9)], scale=0.5, partial=True)
+    assert np.allclose(got, sdpa64(q, k, v, 0.5), rtol=0, atol=1e-12)
+    got = O.sta_forward_explicit(q, k, v, video, tile, [(1, 1, 1)] * 2, scale=0.5, partial=True)
+    coords = O.natural_coords(video)
+    tid = [tuple(int(x) for x in c // np.array(tile)) for c in coords]
+    for t in set(tid):
+        idx = [i for i in range(N) if tid[i] == t]
+        assert np.allclose(got[:, :, idx], sdpa64(q[:, :, idx], k[:, :, idx], v[:, :, idx], 0.5),
+                           rtol=0, atol=1e-12)
