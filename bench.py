@@ -228,7 +228,9 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     q, k, v = make_qkv(w, dev)
-    plan = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    # extents that are not multiples of the tile: partial tiles at the far edges
+    partial = any(e % t for e, t in zip(w.video, w.tile))
+    plan = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim, partial_tiles=partial)
     if args.which == "backward":
         print(json.dumps(backward(args, w, plan, q, k, v, stream)), flush=True)
         return
@@ -289,7 +291,7 @@ def main():
         "roofline": roofline,
     }
 
-    if not args.no_context:
+    if not args.no_context and not partial:
         # explicit reorder -> tile-major forward -> unreorder
         qt, kt, vt = (api.sta_tile_reorder(plan, x) for x in (q, k, v))
         out_t = torch.empty(qt.shape, dtype=torch.float32, device=dev)

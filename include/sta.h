@@ -57,6 +57,9 @@ typedef enum { STA_BF16 = 0, STA_F32 = 1 } sta_dtype;
 
 typedef enum { STA_LAYOUT_NATURAL = 0, STA_LAYOUT_TILE_MAJOR = 1 } sta_layout;
 
+/* Flags of sta_plan_create_ex. */
+enum { STA_PLAN_PARTIAL_TILES = 1 };
+
 typedef struct sta_plan sta_plan; /* opaque, owned by the library */
 
 /* Read-only description of a plan (host memory, filled by sta_plan_get_info). */
@@ -77,6 +80,7 @@ typedef struct {
   int32_t bwd_keys_per_item;    /* keys per dK/dV work item */
   int64_t bwd_items_dq;     /* launched dQ work items (including idle padding) */
   int64_t bwd_items_dkdv;   /* launched dK/dV work items (including idle padding) */
+  int32_t partial_tiles;    /* 1 if some extent is not a multiple of its tile size */
 } sta_plan_info;
 
 /* Build the host plan: tile grid, clamped per-head windows, per-(head, query
@@ -91,6 +95,19 @@ typedef struct {
  * On success *out owns the plan; release it with sta_plan_destroy. */
 sta_status sta_plan_create(int batch, int heads, int T, int H, int W, const int tile[3],
                            const int *window, int head_dim, sta_plan **out);
+
+/* As sta_plan_create, with flags.  STA_PLAN_PARTIAL_TILES accepts extents
+ * that are not multiples of their tile size (the pages leave such latents
+ * open; reading used: an axis then has ceil(extent / tile) tiles, its last
+ * tile partial, windows and tile geometry unchanged, and only tokens that
+ * exist take part -- the same as padding the video to whole tiles and
+ * masking the padded keys).  Such a plan supports sta_forward_plan and
+ * sta_forward_plan_lse in STA_LAYOUT_NATURAL only; sta_plan_perm,
+ * sta_tile_reorder/unreorder, the tile-major layout and sta_backward_plan
+ * return STA_ERR_UNSUPPORTED for it.  Its info.flops counts whole tiles (the
+ * work performed).  STA_ERR_ARG for unknown flags. */
+sta_status sta_plan_create_ex(int batch, int heads, int T, int H, int W, const int tile[3],
+                              const int *window, int head_dim, int flags, sta_plan **out);
 
 /* Release a plan and its device tables (NULL is a no-op).  The caller must
  * make sure no launched work still uses the plan. */

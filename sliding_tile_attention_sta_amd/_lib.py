@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsta.so")
 STA_OK, STA_ERR_ARG, STA_ERR_SHAPE, STA_ERR_UNSUPPORTED, STA_ERR_ALLOC, STA_ERR_HIP = 0, -1, -2, -3, -4, -5
 STA_BF16, STA_F32 = 0, 1
 STA_LAYOUT_NATURAL, STA_LAYOUT_TILE_MAJOR = 0, 1
+STA_PLAN_PARTIAL_TILES = 1
 
 
 class PlanInfo(ctypes.Structure):
@@ -27,7 +28,7 @@ class PlanInfo(ctypes.Structure):
         ("kernel_variant", ctypes.c_int32), ("bwd_supported", ctypes.c_int32),
         ("bwd_queries_per_item", ctypes.c_int32), ("bwd_keys_per_item", ctypes.c_int32),
         ("bwd_items_dq", ctypes.c_int64),
-        ("bwd_items_dkdv", ctypes.c_int64),
+        ("bwd_items_dkdv", ctypes.c_int64), ("partial_tiles", ctypes.c_int32),
     ]
 
 
@@ -41,6 +42,7 @@ _I32P = ctypes.POINTER(ctypes.c_int32)
 SIGNATURES = {
     "sta_plan_create": (_I, [_I, _I, _I, _I, _I, _IP, _IP, _I, ctypes.POINTER(_P)]),
     "sta_plan_destroy": (_I, [_P]),
+    "sta_plan_create_ex": (_I, [_I, _I, _I, _I, _I, _IP, _IP, _I, _I, ctypes.POINTER(_P)]),
     "sta_plan_get_info": (_I, [_P, ctypes.POINTER(PlanInfo)]),
     "sta_plan_perm": (_I, [_P, _I32P, _I64]),
     "sta_plan_kv_tiles": (_I, [_P, _I, _I, _I32P, _I, _IP]),

@@ -51,12 +51,15 @@ class Plan:
     """Owned sta_plan handle (host tables; device tables are uploaded lazily)."""
 
     def __init__(self, batch: int, heads: int, video: Sequence[int], tile: Sequence[int],
-                 windows, head_dim: int):
+                 windows, head_dim: int, partial_tiles: bool = False):
         h = ctypes.c_void_p()
         T, H, W = (int(x) for x in video)
-        st = L.lib().sta_plan_create(int(batch), int(heads), T, H, W, _ints(tile),
-                                     _ints(_flat_windows(windows, heads)), int(head_dim),
-                                     ctypes.byref(h))
+        args = (int(batch), int(heads), T, H, W, _ints(tile), _ints(_flat_windows(windows, heads)),
+                int(head_dim))
+        if partial_tiles:
+            st = L.lib().sta_plan_create_ex(*args, L.STA_PLAN_PARTIAL_TILES, ctypes.byref(h))
+        else:
+            st = L.lib().sta_plan_create(*args, ctypes.byref(h))
         L.check(st, "sta_plan_create")
         self._h = h
         self._destroy = L.lib().sta_plan_destroy

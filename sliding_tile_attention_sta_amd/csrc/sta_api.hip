@@ -35,7 +35,7 @@ sta_status device_tables(const sta_plan *p, DeviceTables *out) {
   for (int j = 0; j < p->V; ++j) off_tm[j] = j;
   const std::vector<int32_t> *parts[] = {&p->kv_off, &p->kv_idx,   &p->sched,    &p->base_nat,
                                          &p->off_nat, &base_tm,     &off_tm,      &p->q_off,
-                                         &p->q_idx,   &p->sched_dq, &p->sched_dkdv};
+                                         &p->q_idx,   &p->sched_dq, &p->sched_dkdv, &p->kmask};
   constexpr int kParts = sizeof(parts) / sizeof(parts[0]);
   size_t offs[kParts], total = 0;
   for (int i = 0; i < kParts; ++i) {
@@ -65,6 +65,7 @@ sta_status device_tables(const sta_plan *p, DeviceTables *out) {
   t.q_idx = reinterpret_cast<int32_t *>(b + offs[8]);
   t.sched_dq = reinterpret_cast<int32_t *>(b + offs[9]);
   t.sched_dkdv = reinterpret_cast<int32_t *>(b + offs[10]);
+  t.kmask = p->kmask.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[11]);
   t.block = block;
   p->dev[dev] = t;
   *out = t;
@@ -79,6 +80,7 @@ sta_status reorder(const sta_plan *p, const void *in, void *out, sta_dtype dtype
   if (!p || !in || !out || !valid_dtype(dtype)) return STA_ERR_ARG;
   const size_t bytes = (size_t)p->batch * p->heads * p->N * p->D * dtype_bytes(dtype);
   if (overlaps(in, bytes, out, bytes)) return STA_ERR_ARG;
+  if (p->partial) return STA_ERR_UNSUPPORTED;   // tile-major order needs whole tiles
   DeviceTables t;
   sta_status st = device_tables(p, &t);
   if (st != STA_OK) return st;
@@ -141,6 +143,7 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   if (!sta::valid_dtype(in_dtype) || !sta::valid_dtype(out_dtype)) return STA_ERR_ARG;
   if (layout != STA_LAYOUT_NATURAL && layout != STA_LAYOUT_TILE_MAJOR) return STA_ERR_ARG;
   if (!(scale > 0.f) || !std::isfinite(scale)) return STA_ERR_ARG;
+  if (p->partial && layout != STA_LAYOUT_NATURAL) return STA_ERR_UNSUPPORTED;
   const size_t elems = (size_t)p->batch * p->heads * p->N * p->D;
   const size_t ib = elems * sta::dtype_bytes(in_dtype), ob = elems * sta::dtype_bytes(out_dtype);
   if (sta::overlaps(out, ob, q, ib) || sta::overlaps(out, ob, k, ib) || sta::overlaps(out, ob, v, ib))
@@ -170,6 +173,7 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   a.n_blocks = (int32_t)p->sched.size();
   a.max_nkv = p->max_nkv;
   a.lse = lse;
+  a.kmask = reinterpret_cast<const uint32_t *>(t.kmask);
   hipError_t e = sta::launch_forward(a, p->variant, p->D, in_dtype == STA_F32, out_dtype == STA_F32,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? STA_OK : STA_ERR_HIP;
@@ -279,7 +283,7 @@ sta_status sta_forward(const void *q, const void *k, const void *v, void *out, i
     if (it != sta::g_cache.end()) {
       p = it->second;
     } else {
-      sta_status st = sta::build_plan(batch, heads, T, H, W, tile, window, head_dim, &p);
+      sta_status st = sta::build_plan(batch, heads, T, H, W, tile, window, head_dim, false, &p);
       if (st != STA_OK) return st;
       try {
         sta::g_cache[key] = p;

@@ -41,6 +41,12 @@
 //   * Rows are located through two small tables (tile base row, tile-local
 //     row offset), so one kernel reads and writes either the natural
 //     [T, H, W] token order or the tile-major order.
+//   * Partial tiles (an extent that is not a multiple of its tile size; a
+//     separate instantiation, PARTIAL): rows are clamped to the tensor, the
+//     scores of keys that do not exist are set to -inf from a per-tile
+//     validity bitmask (one 32-bit word per 32-key block), and queries that
+//     do not exist are not stored.  Only tiles at the video's far edges
+//     hold such tokens.
 
 #include <hip/hip_runtime.h>
 
@@ -71,7 +77,7 @@ __device__ __forceinline__ float swap_sum(float x) {
 }
 
 // D: head dim.  QB: 16-query blocks per wave.  NW: waves per group.
-template <int D, int QB, int NW, bool F32IN, bool F32OUT>
+template <int D, int QB, int NW, bool F32IN, bool F32OUT, bool PARTIAL>
 __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QPI = 16 * QB * NW;               // queries per work item
@@ -113,6 +119,13 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   const int nkv = __builtin_amdgcn_readfirstlane(a.kv_off[h * a.n_tiles + qt + 1]) - kv0;
   for (int i = tid; i < a.V; i += NT) off_l[i] = a.off[i];
   for (int i = tid; i < nkv; i += NT) kvb_l[i] = a.base[a.kv_idx[kv0 + i]];
+  // PARTIAL: the validity word of every 32-key block of the walk.
+  uint32_t *mw_l = reinterpret_cast<uint32_t *>(kvb_l + a.max_nkv);
+  if constexpr (PARTIAL) {
+    const int words = a.V / KB;
+    for (int i = tid; i < nkv * words; i += NT)
+      mw_l[i] = a.kmask[(size_t)a.kv_idx[kv0 + i / words] * words + i % words];
+  }
 
   const char *qg = reinterpret_cast<const char *>(a.q) + (size_t)bh * a.N * D * EB;
   const char *kg = reinterpret_cast<const char *>(a.k) + (size_t)bh * a.N * D * EB;
@@ -125,7 +138,8 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   bf16x8 qf[QB][DC];
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    const int row = qbase + off_l[qloc0 + 16 * j + l16];
+    int row = qbase + off_l[qloc0 + 16 * j + l16];
+    if constexpr (PARTIAL) row = row < a.N ? row : (int)a.N - 1;
 #pragma unroll
     for (int c = 0; c < DC; ++c)
       qf[j][c] = __builtin_bit_cast(bf16x8, as_bf16<F32IN>(load_raw<F32IN>(
@@ -149,6 +163,7 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
       const int c = tid + i * NT;
       if (CHUNKS < NT && c >= CHUNKS) break;
       nrow[i] = tb + off_l[u * KB + c / (D / 8)];
+      if constexpr (PARTIAL) nrow[i] = nrow[i] < a.N ? nrow[i] : (int)a.N - 1;
     }
   };
   auto fetch = [&](Raw8<F32IN>(&dst)[CPT], const char *src, int (&nrow)[CPT], int &ti, int &u) {
@@ -199,6 +214,25 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < QB; ++j)
           st[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[j][c], st[kb][j], 0, 0, 0);
+      }
+    }
+  };
+
+  // PARTIAL: scores of keys that do not exist (block s of the walk) -> -inf;
+  // a block whose keys all exist (every block of an interior tile) skips it.
+  auto mask_block = [&](int s) {
+    if constexpr (PARTIAL) {
+      const uint32_t w = __builtin_amdgcn_readfirstlane(mw_l[s]);
+      if (w != 0xffffffffu) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool ok = (w >> (kb * 16 + 4 * g + r)) & 1u;
+#pragma unroll
+            for (int j = 0; j < QB; ++j)
+              if (!ok) st[kb][j][r] = -INFINITY;
+          }
       }
     }
   };
@@ -312,8 +346,10 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   };
 
   begin_walk();
-  // Initial reference max: each row's max over the first key block.
+  // Initial reference max: each row's max over the first key block (which
+  // always holds an existing key: a tile's first token is inside the video).
   qk(0);
+  mask_block(0);
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     m[j] = swap_max(lane_max(j));
@@ -341,6 +377,7 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     if (grp_a) {
       pvmm((s - 1) & 1);
       qk(s & 1);
+      mask_block(s);
     } else {
       softmax();
     }
@@ -349,6 +386,7 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     } else {
       pvmm((s - 1) & 1);
       qk(s & 1);
+      mask_block(s);
     }
     stash_k(ck, (s + 1) & 1);
     stash_v(cv, s & 1);
@@ -369,6 +407,10 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     const float lsum = swap_sum(l[j]);
     const float inv = 1.f / lsum;
     const int row = qbase + off_l[qloc0 + 16 * j + l16];
+    if constexpr (PARTIAL) {
+      const int ql = qloc0 + 16 * j + l16;
+      if (!((a.kmask[(size_t)qt * spt + ql / 32] >> (ql % 32)) & 1u)) continue;
+    }
     if (a.lse != nullptr && g == 0)
       a.lse[(size_t)bh * a.N + row] = (mb[j] + log2f(lsum)) * 0.69314718055994530942f;
 #pragma unroll
@@ -387,10 +429,10 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
 }
 
 
-template <int D, int QB, int NW, bool FI, bool FO>
+template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL>
 hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
-  auto kern = sta_fwd_kernel<D, QB, NW, FI, FO>;
-  const size_t lds = (size_t)fwd_lds_bytes(D, a.V, a.max_nkv);
+  auto kern = sta_fwd_kernel<D, QB, NW, FI, FO, PARTIAL>;
+  const size_t lds = (size_t)fwd_lds_bytes(D, a.V, a.max_nkv) + (PARTIAL ? 4 * (size_t)a.max_nkv * (a.V / KB) : 0);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -401,10 +443,16 @@ hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int QB, int NW>
+template <int D, int QB, int NW, bool P>
 hipError_t launch_io(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s) {
-  if (f32_in) return f32_out ? launch_one<D, QB, NW, true, true>(a, s) : launch_one<D, QB, NW, true, false>(a, s);
-  return f32_out ? launch_one<D, QB, NW, false, true>(a, s) : launch_one<D, QB, NW, false, false>(a, s);
+  if (f32_in) return f32_out ? launch_one<D, QB, NW, true, true, P>(a, s) : launch_one<D, QB, NW, true, false, P>(a, s);
+  return f32_out ? launch_one<D, QB, NW, false, true, P>(a, s) : launch_one<D, QB, NW, false, false, P>(a, s);
+}
+
+template <int D, int QB, int NW>
+hipError_t launch_p(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s) {
+  if (a.kmask != nullptr) return launch_io<D, QB, NW, true>(a, f32_in, f32_out, s);
+  return launch_io<D, QB, NW, false>(a, f32_in, f32_out, s);
 }
 
 }  // namespace
@@ -413,11 +461,11 @@ hipError_t launch_forward(const FwdArgs &a, int variant, int head_dim, bool f32_
                           hipStream_t stream) {
   if (a.n_blocks <= 0) return hipSuccess;
   if (variant == kTile384) {
-    if (head_dim == 128) return launch_io<128, 3, 8>(a, f32_in, f32_out, stream);
-    return launch_io<64, 3, 8>(a, f32_in, f32_out, stream);
+    if (head_dim == 128) return launch_p<128, 3, 8>(a, f32_in, f32_out, stream);
+    return launch_p<64, 3, 8>(a, f32_in, f32_out, stream);
   }
-  if (head_dim == 128) return launch_io<128, 1, 2>(a, f32_in, f32_out, stream);
-  return launch_io<64, 1, 2>(a, f32_in, f32_out, stream);
+  if (head_dim == 128) return launch_p<128, 1, 2>(a, f32_in, f32_out, stream);
+  return launch_p<64, 1, 2>(a, f32_in, f32_out, stream);
 }
 
 }  // namespace sta

@@ -62,6 +62,7 @@ struct DeviceTables {
   int32_t *q_idx = nullptr;        // query tiles whose window holds each (head, key tile)
   int32_t *sched_dq = nullptr;     // backward dQ work items in launch order (-1 = idle)
   int32_t *sched_dkdv = nullptr;   // backward dK/dV work items in launch order (-1 = idle)
+  int32_t *kmask = nullptr;        // partial plans: n_tiles * tile_tokens/32 validity words
   void *block = nullptr;           // the single allocation holding all of the above
 };
 
@@ -97,6 +98,12 @@ struct sta_plan {
   int32_t bwd_q_subs = 0, bwd_k_subs = 0;   // work items per (b, head, tile)
   bool bwd_ok = false;    // the backward kernels' LDS fits
 
+  // Partial tiles (an extent that is not a multiple of its tile size):
+  // bit i of kmask[tile * V/32 + b] is set iff tile-local token 32b + i
+  // exists.  Empty for plans whose tiles are all whole.
+  bool partial = false;
+  std::vector<int32_t> kmask;
+
   mutable std::mutex mu;
   mutable std::map<int, sta::DeviceTables> dev;   // per HIP device ordinal
 };
@@ -104,8 +111,10 @@ struct sta_plan {
 namespace sta {
 
 // Host-only plan construction (no HIP calls).  Defined in sta_plan.cpp.
+// partial_ok: accept extents that are not multiples of their tile size
+// (the last tile of such an axis is partial; forward in natural layout only).
 sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[3],
-                      const int *window, int head_dim, sta_plan **out);
+                      const int *window, int head_dim, bool partial_ok, sta_plan **out);
 
 // Releases device tables; defined in sta_api.hip (needs HIP).
 void release_device_tables(sta_plan *plan);

@@ -21,6 +21,7 @@ struct FwdArgs {
   int32_t n_blocks;        // length of sched
   int32_t max_nkv;         // longest key-tile list of any (head, query tile)
   float *lse;              // NULL, or [batch, heads, N] row log-sum-exp (natural log)
+  const uint32_t *kmask;   // NULL (whole tiles), or per tile V/32 words of token validity
 };
 
 // Launch the forward kernel.  variant: 0 generic, 1 384-query items.

@@ -68,7 +68,7 @@ std::vector<int32_t> build_schedule(const sta_plan *p, const std::vector<int32_t
 }  // namespace
 
 sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[3],
-                      const int *window, int head_dim, sta_plan **out) {
+                      const int *window, int head_dim, bool partial_ok, sta_plan **out) {
   if (!out || !tile || !window) return STA_ERR_ARG;
   *out = nullptr;
   if (batch < 1 || heads < 1 || T < 1 || H < 1 || W < 1) return STA_ERR_ARG;
@@ -78,7 +78,7 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
     if (window[i] < 1) return STA_ERR_ARG;
   const int ext[3] = {T, H, W};
   for (int d = 0; d < 3; ++d)
-    if (ext[d] % tile[d] != 0) return STA_ERR_SHAPE;
+    if (ext[d] % tile[d] != 0 && !partial_ok) return STA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return STA_ERR_UNSUPPORTED;
   const int64_t V64 = (int64_t)tile[0] * tile[1] * tile[2];
   if (V64 % kKeyBlock != 0 || V64 > kMaxTileTokens) return STA_ERR_UNSUPPORTED;
@@ -90,7 +90,11 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
   if (!p) return STA_ERR_ALLOC;
   try {
     p->batch = batch; p->heads = heads; p->T = T; p->H = H; p->W = W; p->D = head_dim;
-    for (int d = 0; d < 3; ++d) { p->tile[d] = tile[d]; p->grid[d] = ext[d] / tile[d]; }
+    for (int d = 0; d < 3; ++d) {
+      p->tile[d] = tile[d];
+      p->grid[d] = (ext[d] + tile[d] - 1) / tile[d];
+      if (ext[d] % tile[d] != 0) p->partial = true;
+    }
     p->V = (int32_t)V64;
     p->N = N64;
     p->n_tiles = p->grid[0] * p->grid[1] * p->grid[2];
@@ -134,7 +138,8 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
       p->max_nkv = std::max(p->max_nkv, p->kv_off[i + 1] - p->kv_off[i]);
     // The forward kernel keeps two K and two V stages of 32 keys plus the
     // tile-local row offsets and the item's key-tile rows in LDS (160 KiB).
-    if (fwd_lds_bytes(head_dim, p->V, p->max_nkv) > kMaxLds) {
+    if (fwd_lds_bytes(head_dim, p->V, p->max_nkv) + (p->partial ? 4LL * p->max_nkv * (p->V / kKeyBlock) : 0) >
+        kMaxLds) {
       delete p;
       return STA_ERR_UNSUPPORTED;
     }
@@ -149,6 +154,20 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
     for (int j = 0; j < p->V; ++j) {
       const int lt = j / (tile[1] * tile[2]), ly = (j / tile[2]) % tile[1], lz = j % tile[2];
       p->off_nat[j] = (lt * H + ly) * W + lz;
+    }
+    if (p->partial) {
+      // Token validity per tile; with partial tiles base + off can name a
+      // row past the tile's edge (or past the tensor), which the kernel
+      // clamps and masks.
+      p->kmask.assign((size_t)p->n_tiles * (p->V / 32), 0);
+      for (int t = 0; t < p->n_tiles; ++t) {
+        const int ct = t / (nH * nW), cy = (t / nW) % nH, cz = t % nW;
+        for (int j = 0; j < p->V; ++j) {
+          const int lt = j / (tile[1] * tile[2]), ly = (j / tile[2]) % tile[1], lz = j % tile[2];
+          if (ct * tile[0] + lt < T && cy * tile[1] + ly < H && cz * tile[2] + lz < W)
+            p->kmask[(size_t)t * (p->V / 32) + j / 32] |= (int32_t)(1u << (j % 32));
+        }
+      }
     }
     p->sched = build_schedule(p, p->kv_off, p->subs);
 
@@ -178,7 +197,7 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
 #endif
     p->bwd_q_subs = p->V / (32 * p->bwd_q_waves);
     p->bwd_k_subs = p->V / (32 * p->bwd_k_pairs);
-    p->bwd_ok = bwd_lds_bytes(head_dim, p->V, std::max(p->max_nkv, p->max_nq)) <= kMaxLds;
+    p->bwd_ok = !p->partial && bwd_lds_bytes(head_dim, p->V, std::max(p->max_nkv, p->max_nq)) <= kMaxLds;
     if (p->bwd_ok) {
       p->sched_dq = build_schedule(p, p->kv_off, p->bwd_q_subs);
       p->sched_dkdv = build_schedule(p, p->q_off, p->bwd_k_subs);
@@ -197,7 +216,14 @@ extern "C" {
 
 sta_status sta_plan_create(int batch, int heads, int T, int H, int W, const int tile[3],
                            const int *window, int head_dim, sta_plan **out) {
-  return sta::build_plan(batch, heads, T, H, W, tile, window, head_dim, out);
+  return sta::build_plan(batch, heads, T, H, W, tile, window, head_dim, false, out);
+}
+
+sta_status sta_plan_create_ex(int batch, int heads, int T, int H, int W, const int tile[3],
+                              const int *window, int head_dim, int flags, sta_plan **out) {
+  if (flags & ~STA_PLAN_PARTIAL_TILES) return STA_ERR_ARG;
+  return sta::build_plan(batch, heads, T, H, W, tile, window, head_dim,
+                         (flags & STA_PLAN_PARTIAL_TILES) != 0, out);
 }
 
 sta_status sta_plan_destroy(sta_plan *plan) {
@@ -226,11 +252,13 @@ sta_status sta_plan_get_info(const sta_plan *p, sta_plan_info *info) {
   info->bwd_keys_per_item = 32 * p->bwd_k_pairs;
   info->bwd_items_dq = (int64_t)p->sched_dq.size();
   info->bwd_items_dkdv = (int64_t)p->sched_dkdv.size();
+  info->partial_tiles = p->partial ? 1 : 0;
   return STA_OK;
 }
 
 sta_status sta_plan_perm(const sta_plan *p, int32_t *perm, int64_t cap) {
   if (!p || !perm || cap < p->N) return STA_ERR_ARG;
+  if (p->partial) return STA_ERR_UNSUPPORTED;
   for (int qt = 0; qt < p->n_tiles; ++qt)
     for (int j = 0; j < p->V; ++j) perm[(int64_t)qt * p->V + j] = p->base_nat[qt] + p->off_nat[j];
   return STA_OK;

@@ -77,6 +77,15 @@ WORKLOADS = {
                      magnitude=(0.5, 4.0),
                      description="60x48x80 latent (230400 tokens), tile 6x8x8, window 3x3x3, "
                                  "24 heads, d128, bf16, per-token magnitude U(0.5, 4)"),
+    # Extents that are not multiples of the tile (partial tiles at the far
+    # edges): the exact 720p latent (720 / 16 = 45 rows) and a small case
+    # with partial tiles on every axis.
+    "720p-exact": Workload("720p-exact", 8, (30, 45, 80), (6, 8, 8), ((3, 3, 3),) * 24, 128, "bf16",
+                           description="30x45x80 latent (108000 tokens), tile 6x8x8 (last row of "
+                                       "tiles holds 5 of 8 rows), window 3x3x3, 24 heads, d128, bf16"),
+    "partial-small": Workload("partial-small", 9, (5, 13, 11), (2, 4, 4), ((3, 3, 3), (1, 2, 5)), 64,
+                              "f32", description="5x13x11 latent, tile 2x4x4 (partial on every "
+                                                 "axis), windows 3x3x3 and 1x2x5, 2 heads, d64, fp32"),
     # 2D STA (an image latent: T = 1, tiles of one frame)
     "2d": Workload("2d", 6, (1, 96, 96), (1, 16, 24), ((1, 3, 3),) * 8, 128, "bf16",
                    description="2D: 96x96 latent, tile 16x24 (384 tokens), window 3x3 tiles, "

@@ -309,3 +309,40 @@ def test_window_search_argument_errors():
     assert lib.sta_window_select(0, _ints([3, 4, 4]), c, 2, err, 0.1, out) == L.STA_ERR_ARG
     cnt = ctypes.c_int()
     assert lib.sta_window_candidates(_ints([0, 1, 1]), None, 0, ctypes.byref(cnt)) == L.STA_ERR_ARG
+
+
+# ---------------------------------------------------------------------------
+# Partial tiles (extents that are not multiples of the tile size)
+# ---------------------------------------------------------------------------
+
+def test_partial_plan_geometry_and_unsupported_paths():
+    video, tile, window = (30, 45, 80), (6, 8, 8), (3, 3, 3)
+    assert _create(1, 2, *video, _ints(list(tile)), _ints(list(window) * 2), 128) == L.STA_ERR_SHAPE
+    p = api.Plan(1, 2, video, tile, [window], 128, partial_tiles=True)
+    info = p.info
+    grid = O.tile_grid(video, tile, partial=True)
+    assert tuple(info.grid) == grid == (5, 6, 10)
+    assert info.partial_tiles == 1 and info.bwd_supported == 0
+    nT, nH, nW = grid
+    for qt in range(0, nT * nH * nW, 3):
+        c = (qt // (nH * nW), (qt // nW) % nH, qt % nW)
+        (t0, t1), (y0, y1), (z0, z1) = O.window_tiles(c, window, grid)
+        want = sorted((a * nH + b) * nW + cc for a in range(t0, t1) for b in range(y0, y1)
+                      for cc in range(z0, z1))
+        assert p.kv_tiles(0, qt) == want
+    lib = L.lib()
+    P = ctypes.c_void_p
+    q, k, v, o = P(1 << 40), P(2 << 40), P(3 << 40), P(4 << 40)
+    buf = (ctypes.c_int32 * info.tokens)()
+    assert lib.sta_plan_perm(p.handle, buf, info.tokens) == L.STA_ERR_UNSUPPORTED
+    assert lib.sta_tile_reorder(p.handle, q, o, 0, None) == L.STA_ERR_UNSUPPORTED
+    assert lib.sta_forward_plan(p.handle, q, k, v, o, 0.125, 0, 1, L.STA_LAYOUT_TILE_MAJOR, None) == L.STA_ERR_UNSUPPORTED
+    g, lse, dl, dq, dk, dv = (P(i << 40) for i in range(5, 11))
+    assert lib.sta_backward_plan(p.handle, q, k, v, o, g, lse, dl, dq, dk, dv, 0.125, 0, 1, 1, 0,
+                                 None) == L.STA_ERR_UNSUPPORTED
+    h = ctypes.c_void_p()
+    assert lib.sta_plan_create_ex(1, 2, *video, _ints(list(tile)), _ints(list(window) * 2), 128, 6,
+                                  ctypes.byref(h)) == L.STA_ERR_ARG
+    # whole tiles through the flag: an ordinary plan
+    q2 = api.Plan(1, 2, (30, 48, 80), tile, [window], 128, partial_tiles=True)
+    assert q2.info.partial_tiles == 0 and q2.info.bwd_supported == 1
