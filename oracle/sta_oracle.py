@@ -36,7 +36,7 @@ design notes of the repository):
   R4  scale defaults to 1/sqrt(head_dim).
   R5  Inputs are taken exactly as given (for bf16 workloads: the bf16 values,
       widened); all arithmetic here is float64.
-  R7  (Only when asked for, ``partial=True``.)  An extent that is not a
+  R11 (Only when asked for, ``partial=True``.)  An extent that is not a
       multiple of its tile size gets ceil(extent / tile) tiles; the last tile
       on that axis is partial.  Tile coordinates, windows and the tile-level
       mask are unchanged; only tokens that exist take part.  This equals
@@ -78,7 +78,7 @@ __all__ = [
 def tile_grid(video: Sequence[int], tile: Sequence[int], partial: bool = False) -> tuple[int, int, int]:
     """Number of tiles along (T, H, W).  Tiles do not overlap and cover the
     video, so every extent must be a multiple of its tile size -- unless
-    partial is set (reading R7): then an axis has ceil(extent / tile) tiles
+    partial is set (reading R11): then an axis has ceil(extent / tile) tiles
     and its last tile holds only the tokens that exist."""
     if len(video) != 3 or len(tile) != 3:
         raise ValueError("video and tile must have three axes (T, H, W)")
@@ -227,7 +227,7 @@ def sta_forward_query_tiles(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     box of tiles on each axis, is the box of tokens
     [s_t*tT, (s_t+w_t)*tT) x [s_y*tH, ...) x [s_z*tW, ...).
     Returns, per query tile, float64 [tT, tH, tW, D] in natural order
-    (smaller for a partial tile, reading R7: slices stop at the video's end).
+    (smaller for a partial tile, reading R11: slices stop at the video's end).
     """
     _, _, T, H, W, D = q.shape
     grid = tile_grid((T, H, W), tile, partial)

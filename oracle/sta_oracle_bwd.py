@@ -23,9 +23,10 @@ written out here in float64:
   dq_i  = scale * sum_j dz_ij k_j
   dk_j  = scale * sum_i dz_ij q_i
 
-Readings R1-R5 of the forward oracle apply unchanged.  One more:
+Readings R1-R5 of the forward oracle apply unchanged.  One more (numbered
+as in the design notes):
 
-  R6  The row log-sum-exp is reported in natural-log units over the
+  R10 The row log-sum-exp is reported in natural-log units over the
       permitted keys of the row, with the scale applied (lse_i above).
 
 Parity pins (``tests/test_oracle_bwd_pins.py``): central finite differences

@@ -437,7 +437,7 @@ def test_token_predicate_matches_bruteforce():
 
 
 # ---------------------------------------------------------------------------
-# Partial tiles (reading R7: extents that are not multiples of the tile)
+# Partial tiles (reading R11: extents that are not multiples of the tile)
 # ---------------------------------------------------------------------------
 
 def bf_keys_partial(qx, video, tile, window):
