@@ -35,9 +35,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "search"], default="forward",
-                    help="forward (the metric line), backward (delta + dQ + dK/dV kernels) or "
-                         "search (per-head window search over the default candidates)")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "search", "swa"],
+                    default="forward",
+                    help="forward (the metric line), backward (delta + dQ + dK/dV kernels), "
+                         "search (per-head window search over the default candidates) or swa "
+                         "(token-wise sliding window attention with the same keys per query, "
+                         "against STA on the same inputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -201,6 +204,60 @@ def search(args, w, stream):
     }
 
 
+def swa(args, w, plan, q, k, v, stream):
+    """Token-wise 3D sliding window attention on the workload's inputs, each
+    query's window sized so that it holds as many keys as STA's window
+    (wT * tT x wH * tH x wW * tW tokens), timed beside STA on the same
+    inputs.  Both compute the same algorithmic FLOPs; SWA walks the union of
+    a query tile's windows with per-score masks."""
+    import torch
+    from sliding_tile_attention_sta_amd import api
+
+    toks = [tuple(a * t for a, t in zip(win, w.tile)) for win in w.windows]
+    splan = api.Plan(w.batch, w.heads, w.video, w.tile, toks, w.head_dim, token_windows=True)
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ms_swa = timed(lambda: api.sta_forward_plan(splan, q, k, v, out=out, scale=w.scale, stream=stream),
+                   args.steps, args.warmup, stream)
+    ms_sta = timed(lambda: api.sta_forward_plan(plan, q, k, v, out=out, scale=w.scale, stream=stream),
+                   args.steps, args.warmup, stream)
+    # executed key blocks of the SWA walk: rows of the union box x 32-key runs
+    def start(x, wd, e):
+        return min(max(x - (wd - 1) // 2, 0), e - wd)
+    grid = [e // t for e, t in zip(w.video, w.tile)]
+    V = w.tile[0] * w.tile[1] * w.tile[2]
+    blocks = 0
+    for win in toks:
+        wc = [min(a, e) for a, e in zip(win, w.video)]
+        span = []
+        for d in range(3):
+            per = []
+            for c in range(grid[d]):
+                lo = start(c * w.tile[d], wc[d], w.video[d])
+                hi = start(c * w.tile[d] + w.tile[d] - 1, wc[d], w.video[d]) + wc[d]
+                per.append(hi - lo)
+            span.append(per)
+        for a in span[0]:
+            for b in span[1]:
+                for c in span[2]:
+                    blocks += a * b * ((c + 31) // 32)
+    executed = 4.0 * blocks * 32 * V * w.head_dim * w.batch
+    fl_swa = splan.flops
+    return {
+        "metric": "token-wise SWA fwd ms vs STA fwd ms, same keys per query",
+        "value": round(ms_swa / ms_sta, 3), "unit": "SWA time / STA time", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_swa, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "video": list(w.video), "tile": list(w.tile),
+                   "sta_windows_tiles": sorted({tuple(x) for x in w.windows}),
+                   "swa_windows_tokens": sorted(set(toks)), "heads": w.heads, "head_dim": w.head_dim},
+        "swa": {"ms": round(ms_swa, 4), "tflops_algorithmic": round(fl_swa / (ms_swa * 1e-3) / 1e12, 1),
+                "executed_over_algorithmic": round(executed / fl_swa, 3),
+                "tflops_executed": round(executed / (ms_swa * 1e-3) / 1e12, 1)},
+        "sta": {"ms": round(ms_sta, 4), "tflops": round(plan.flops / (ms_sta * 1e-3) / 1e12, 1)},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -237,6 +294,9 @@ def main():
     if args.which == "search":
         del q, k, v
         print(json.dumps(search(args, w, stream)), flush=True)
+        return
+    if args.which == "swa":
+        print(json.dumps(swa(args, w, plan, q, k, v, stream)), flush=True)
         return
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     flops = plan.flops

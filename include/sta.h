@@ -81,6 +81,7 @@ typedef struct {
   int64_t bwd_items_dq;     /* launched dQ work items (including idle padding) */
   int64_t bwd_items_dkdv;   /* launched dK/dV work items (including idle padding) */
   int32_t partial_tiles;    /* 1 if some extent is not a multiple of its tile size */
+  int32_t swa;              /* 1 for a token-wise sliding-window plan (sta_swa_plan_create) */
 } sta_plan_info;
 
 /* Build the host plan: tile grid, clamped per-head windows, per-(head, query
@@ -108,6 +109,22 @@ sta_status sta_plan_create(int batch, int heads, int T, int H, int W, const int 
  * work performed).  STA_ERR_ARG for unknown flags. */
 sta_status sta_plan_create_ex(int batch, int heads, int T, int H, int W, const int tile[3],
                               const int *window, int head_dim, int flags, sta_plan **out);
+
+/* Token-wise 3D sliding window attention, the baseline the pages contrast
+ * STA with (index page, Abstract; gptget summary page, Methodology and
+ * Novelty): every query token attends to the keys of its own window of
+ * window_tokens[3h .. 3h+2] tokens (per head; clamped to the extents),
+ * centred on it and shifted inward at the borders (the same rule as STA's
+ * window, at token level).  The plan groups queries into work items of
+ * tile[3] tokens (extents must be multiples of it); a work item walks the
+ * union of its queries' windows in runs of 32 keys and masks every score
+ * against its query's window, so its blocks are "mixed".  Run it with
+ * sta_forward_plan / sta_forward_plan_lse in STA_LAYOUT_NATURAL;
+ * info.flops counts the permitted (query, key) pairs only.  Tile-major
+ * layout, reorder, perm and backward return STA_ERR_UNSUPPORTED.
+ * Errors: as sta_plan_create. */
+sta_status sta_swa_plan_create(int batch, int heads, int T, int H, int W, const int tile[3],
+                               const int *window_tokens, int head_dim, sta_plan **out);
 
 /* Release a plan and its device tables (NULL is a no-op).  The caller must
  * make sure no launched work still uses the plan. */

@@ -29,6 +29,7 @@ class PlanInfo(ctypes.Structure):
         ("bwd_queries_per_item", ctypes.c_int32), ("bwd_keys_per_item", ctypes.c_int32),
         ("bwd_items_dq", ctypes.c_int64),
         ("bwd_items_dkdv", ctypes.c_int64), ("partial_tiles", ctypes.c_int32),
+        ("swa", ctypes.c_int32),
     ]
 
 
@@ -43,6 +44,7 @@ SIGNATURES = {
     "sta_plan_create": (_I, [_I, _I, _I, _I, _I, _IP, _IP, _I, ctypes.POINTER(_P)]),
     "sta_plan_destroy": (_I, [_P]),
     "sta_plan_create_ex": (_I, [_I, _I, _I, _I, _I, _IP, _IP, _I, _I, ctypes.POINTER(_P)]),
+    "sta_swa_plan_create": (_I, [_I, _I, _I, _I, _I, _IP, _IP, _I, ctypes.POINTER(_P)]),
     "sta_plan_get_info": (_I, [_P, ctypes.POINTER(PlanInfo)]),
     "sta_plan_perm": (_I, [_P, _I32P, _I64]),
     "sta_plan_kv_tiles": (_I, [_P, _I, _I, _I32P, _I, _IP]),

@@ -51,12 +51,16 @@ class Plan:
     """Owned sta_plan handle (host tables; device tables are uploaded lazily)."""
 
     def __init__(self, batch: int, heads: int, video: Sequence[int], tile: Sequence[int],
-                 windows, head_dim: int, partial_tiles: bool = False):
+                 windows, head_dim: int, partial_tiles: bool = False, token_windows: bool = False):
+        """token_windows=True: a token-wise sliding-window (SWA) plan whose
+        windows are in tokens; tile then only groups queries into work items."""
         h = ctypes.c_void_p()
         T, H, W = (int(x) for x in video)
         args = (int(batch), int(heads), T, H, W, _ints(tile), _ints(_flat_windows(windows, heads)),
                 int(head_dim))
-        if partial_tiles:
+        if token_windows:
+            st = L.lib().sta_swa_plan_create(*args, ctypes.byref(h))
+        elif partial_tiles:
             st = L.lib().sta_plan_create_ex(*args, L.STA_PLAN_PARTIAL_TILES, ctypes.byref(h))
         else:
             st = L.lib().sta_plan_create(*args, ctypes.byref(h))

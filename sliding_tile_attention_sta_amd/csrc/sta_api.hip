@@ -35,7 +35,8 @@ sta_status device_tables(const sta_plan *p, DeviceTables *out) {
   for (int j = 0; j < p->V; ++j) off_tm[j] = j;
   const std::vector<int32_t> *parts[] = {&p->kv_off, &p->kv_idx,   &p->sched,    &p->base_nat,
                                          &p->off_nat, &base_tm,     &off_tm,      &p->q_off,
-                                         &p->q_idx,   &p->sched_dq, &p->sched_dkdv, &p->kmask};
+                                         &p->q_idx,   &p->sched_dq, &p->sched_dkdv, &p->kmask,
+                                         &p->swin};
   constexpr int kParts = sizeof(parts) / sizeof(parts[0]);
   size_t offs[kParts], total = 0;
   for (int i = 0; i < kParts; ++i) {
@@ -66,6 +67,7 @@ sta_status device_tables(const sta_plan *p, DeviceTables *out) {
   t.sched_dq = reinterpret_cast<int32_t *>(b + offs[9]);
   t.sched_dkdv = reinterpret_cast<int32_t *>(b + offs[10]);
   t.kmask = p->kmask.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[11]);
+  t.swin = p->swin.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[12]);
   t.block = block;
   p->dev[dev] = t;
   *out = t;
@@ -80,7 +82,7 @@ sta_status reorder(const sta_plan *p, const void *in, void *out, sta_dtype dtype
   if (!p || !in || !out || !valid_dtype(dtype)) return STA_ERR_ARG;
   const size_t bytes = (size_t)p->batch * p->heads * p->N * p->D * dtype_bytes(dtype);
   if (overlaps(in, bytes, out, bytes)) return STA_ERR_ARG;
-  if (p->partial) return STA_ERR_UNSUPPORTED;   // tile-major order needs whole tiles
+  if (p->partial || p->swa) return STA_ERR_UNSUPPORTED;   // tile-major order needs whole tiles
   DeviceTables t;
   sta_status st = device_tables(p, &t);
   if (st != STA_OK) return st;
@@ -143,7 +145,7 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   if (!sta::valid_dtype(in_dtype) || !sta::valid_dtype(out_dtype)) return STA_ERR_ARG;
   if (layout != STA_LAYOUT_NATURAL && layout != STA_LAYOUT_TILE_MAJOR) return STA_ERR_ARG;
   if (!(scale > 0.f) || !std::isfinite(scale)) return STA_ERR_ARG;
-  if (p->partial && layout != STA_LAYOUT_NATURAL) return STA_ERR_UNSUPPORTED;
+  if ((p->partial || p->swa) && layout != STA_LAYOUT_NATURAL) return STA_ERR_UNSUPPORTED;
   const size_t elems = (size_t)p->batch * p->heads * p->N * p->D;
   const size_t ib = elems * sta::dtype_bytes(in_dtype), ob = elems * sta::dtype_bytes(out_dtype);
   if (sta::overlaps(out, ob, q, ib) || sta::overlaps(out, ob, k, ib) || sta::overlaps(out, ob, v, ib))
@@ -174,6 +176,10 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   a.max_nkv = p->max_nkv;
   a.lse = lse;
   a.kmask = reinterpret_cast<const uint32_t *>(t.kmask);
+  a.swin = t.swin;
+  a.T = p->T; a.H = p->H; a.W = p->W;
+  a.tT = p->tile[0]; a.tH = p->tile[1]; a.tW = p->tile[2];
+  a.gH = p->grid[1]; a.gW = p->grid[2];
   hipError_t e = sta::launch_forward(a, p->variant, p->D, in_dtype == STA_F32, out_dtype == STA_F32,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? STA_OK : STA_ERR_HIP;

@@ -47,6 +47,14 @@
 //     validity bitmask (one 32-bit word per 32-key block), and queries that
 //     do not exist are not stored.  Only tiles at the video's far edges
 //     hold such tokens.
+//   * Token-wise sliding window attention (SWA, a separate instantiation):
+//     the baseline STA is contrasted with, for measurement.  Each query has
+//     its own window of tokens centred on itself (shifted inward at the
+//     borders); a query tile walks the union of its queries' windows in
+//     runs of 32 keys along W, and every score is masked against its
+//     query's window.  The row's reference max starts at the query's score
+//     against its own key, which every window holds (the first key block
+//     may hold none of a query's keys).
 
 #include <hip/hip_runtime.h>
 
@@ -76,8 +84,15 @@ __device__ __forceinline__ float swap_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Token-wise SWA: first token of the w-token window of coordinate x on an
+// axis of extent e (w <= e).
+__device__ __forceinline__ int tok_start(int x, int w, int e) {
+  const int s = x - (w - 1) / 2;
+  return s < 0 ? 0 : (s > e - w ? e - w : s);
+}
+
 // D: head dim.  QB: 16-query blocks per wave.  NW: waves per group.
-template <int D, int QB, int NW, bool F32IN, bool F32OUT, bool PARTIAL>
+template <int D, int QB, int NW, bool F32IN, bool F32OUT, bool PARTIAL, bool SWA = false>
 __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QPI = 16 * QB * NW;               // queries per work item
@@ -115,10 +130,29 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
 
   // Work-item constants are wave-uniform; readfirstlane keeps them in SGPRs
   // so that the key loop is a scalar (non-divergent) loop.
-  const int kv0 = __builtin_amdgcn_readfirstlane(a.kv_off[h * a.n_tiles + qt]);
-  const int nkv = __builtin_amdgcn_readfirstlane(a.kv_off[h * a.n_tiles + qt + 1]) - kv0;
+  int kv0 = 0, nkv = 0;
+  if constexpr (!SWA) {
+    kv0 = __builtin_amdgcn_readfirstlane(a.kv_off[h * a.n_tiles + qt]);
+    nkv = __builtin_amdgcn_readfirstlane(a.kv_off[h * a.n_tiles + qt + 1]) - kv0;
+  }
   for (int i = tid; i < a.V; i += NT) off_l[i] = a.off[i];
   for (int i = tid; i < nkv; i += NT) kvb_l[i] = a.base[a.kv_idx[kv0 + i]];
+  // SWA: the union box of the tile's query windows, walked as rows (t, y)
+  // of nzb runs of 32 keys starting at z = z_lo.
+  int s_wt = 0, s_wy = 0, s_wz = 0, s_tlo = 0, s_ylo = 0, s_zlo = 0, s_ny = 1, s_nzb = 1, s_nrows = 0;
+  if constexpr (SWA) {
+    s_wt = a.swin[3 * h]; s_wy = a.swin[3 * h + 1]; s_wz = a.swin[3 * h + 2];
+    const int ct = qt / (a.gH * a.gW), cy = (qt / a.gW) % a.gH, cz = qt % a.gW;
+    s_tlo = tok_start(ct * a.tT, s_wt, a.T);
+    s_ylo = tok_start(cy * a.tH, s_wy, a.H);
+    s_zlo = tok_start(cz * a.tW, s_wz, a.W);
+    const int thi = tok_start(ct * a.tT + a.tT - 1, s_wt, a.T) + s_wt;
+    const int yhi = tok_start(cy * a.tH + a.tH - 1, s_wy, a.H) + s_wy;
+    const int zhi = tok_start(cz * a.tW + a.tW - 1, s_wz, a.W) + s_wz;
+    s_ny = yhi - s_ylo;
+    s_nzb = (zhi - s_zlo + KB - 1) / KB;
+    s_nrows = (thi - s_tlo) * s_ny;
+  }
   // PARTIAL: the validity word of every 32-key block of the walk.
   uint32_t *mw_l = reinterpret_cast<uint32_t *>(kvb_l + a.max_nkv);
   if constexpr (PARTIAL) {
@@ -147,8 +181,8 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   }
 
   // ---- key-tile walk ------------------------------------------------------
-  const int spt = a.V / KB;        // steps per key tile
-  const int nsteps = nkv * spt;
+  const int spt = SWA ? s_nzb : a.V / KB;   // steps per key tile (SWA: per key row)
+  const int nsteps = SWA ? s_nrows * s_nzb : nkv * spt;
 
   // Global -> register prefetch of one 32-key block of K and of V.  The rows
   // of the next fetch are looked up (LDS tables) right after the current one
@@ -157,6 +191,21 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   int fk_ti = 0, fk_u = 0, fv_ti = 0, fv_u = 0;   // key tile / step-in-tile of the next fetch
   int krow[CPT], vrow[CPT];                        // token rows of the next fetch
   auto rows_at = [&](int (&nrow)[CPT], int ti, int u) {
+    if constexpr (SWA) {
+      // ti = key row (t, y) of the union box, u = 32-key run along z; past
+      // the last block the last one is re-read.
+      if (ti >= s_nrows) { ti = s_nrows - 1; u = s_nzb - 1; }
+      const int r0 = ((s_tlo + ti / s_ny) * a.H + s_ylo + ti % s_ny) * a.W;
+      const int z0 = s_zlo + u * KB;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * NT;
+        if (CHUNKS < NT && c >= CHUNKS) break;
+        const int z = z0 + c / (D / 8);
+        nrow[i] = r0 + (z < a.W ? z : a.W - 1);
+      }
+      return;
+    }
     const int tb = kvb_l[ti < nkv ? ti : nkv - 1];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -233,6 +282,39 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
             for (int j = 0; j < QB; ++j)
               if (!ok) st[kb][j][r] = -INFINITY;
           }
+      }
+    }
+  };
+
+  // SWA: per lane and query block, the query's window starts; the current
+  // block's key row (t, y) and z of its first key.
+  int swq[QB][3];
+  int cur_row = 0, cur_u = 0;
+  if constexpr (SWA) {
+    const int ct = qt / (a.gH * a.gW), cy = (qt / a.gW) % a.gH, cz = qt % a.gW;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      const int loc = qloc0 + 16 * j + l16;
+      const int lt = loc / (a.tH * a.tW), ly = (loc / a.tW) % a.tH, lz = loc % a.tW;
+      swq[j][0] = tok_start(ct * a.tT + lt, s_wt, a.T);
+      swq[j][1] = tok_start(cy * a.tH + ly, s_wy, a.H);
+      swq[j][2] = tok_start(cz * a.tW + lz, s_wz, a.W);
+    }
+  }
+  // SWA: scores outside each query's own window -> -inf (block s, whose
+  // position the step keeps in cur_row / cur_u).
+  auto mask_swa = [&]() {
+    if constexpr (SWA) {
+      const int t = s_tlo + cur_row / s_ny, y = s_ylo + cur_row % s_ny, z0 = s_zlo + cur_u * KB;
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const bool ty = (unsigned)(t - swq[j][0]) < (unsigned)s_wt && (unsigned)(y - swq[j][1]) < (unsigned)s_wy;
+        const int zr = z0 + 4 * g - swq[j][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (!(ty && (unsigned)(zr + kb * 16 + r) < (unsigned)s_wz)) st[kb][j][r] = -INFINITY;
       }
     }
   };
@@ -348,11 +430,28 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   begin_walk();
   // Initial reference max: each row's max over the first key block (which
   // always holds an existing key: a tile's first token is inside the video).
-  qk(0);
-  mask_block(0);
+  // SWA: the query's score against its own key.
+  if constexpr (SWA) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      const int row = qbase + off_l[qloc0 + 16 * j + l16];
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8 kx = __builtin_bit_cast(bf16x8, as_bf16<F32IN>(load_raw<F32IN>(
+                                                 kg + ((size_t)row * D + 32 * c + 8 * g) * EB)));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)qf[j][c][e], (float)kx[e], acc);
+      }
+      m[j] = swap_sum(acc);
+    }
+  } else {
+    qk(0);
+    mask_block(0);
+  }
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    m[j] = swap_max(lane_max(j));
+    if constexpr (!SWA) m[j] = swap_max(lane_max(j));
     mb[j] = m[j] * sl2e;
     l[j] = 0.f;
 #pragma unroll
@@ -378,6 +477,7 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
       pvmm((s - 1) & 1);
       qk(s & 1);
       mask_block(s);
+      mask_swa();
     } else {
       softmax();
     }
@@ -387,6 +487,10 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
       pvmm((s - 1) & 1);
       qk(s & 1);
       mask_block(s);
+      mask_swa();
+    }
+    if constexpr (SWA) {
+      if (++cur_u == s_nzb) { cur_u = 0; ++cur_row; }
     }
     stash_k(ck, (s + 1) & 1);
     stash_v(cv, s & 1);
@@ -429,9 +533,9 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
 }
 
 
-template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL>
+template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL, bool SWA = false>
 hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
-  auto kern = sta_fwd_kernel<D, QB, NW, FI, FO, PARTIAL>;
+  auto kern = sta_fwd_kernel<D, QB, NW, FI, FO, PARTIAL, SWA>;
   const size_t lds = (size_t)fwd_lds_bytes(D, a.V, a.max_nkv) + (PARTIAL ? 4 * (size_t)a.max_nkv * (a.V / KB) : 0);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   if (lds > 64 * 1024) {
@@ -451,6 +555,12 @@ hipError_t launch_io(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s)
 
 template <int D, int QB, int NW>
 hipError_t launch_p(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s) {
+  if (a.swin != nullptr) {
+    if (f32_in) return f32_out ? launch_one<D, QB, NW, true, true, false, true>(a, s)
+                               : launch_one<D, QB, NW, true, false, false, true>(a, s);
+    return f32_out ? launch_one<D, QB, NW, false, true, false, true>(a, s)
+                   : launch_one<D, QB, NW, false, false, false, true>(a, s);
+  }
   if (a.kmask != nullptr) return launch_io<D, QB, NW, true>(a, f32_in, f32_out, s);
   return launch_io<D, QB, NW, false>(a, f32_in, f32_out, s);
 }

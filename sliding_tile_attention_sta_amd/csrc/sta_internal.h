@@ -63,6 +63,7 @@ struct DeviceTables {
   int32_t *sched_dq = nullptr;     // backward dQ work items in launch order (-1 = idle)
   int32_t *sched_dkdv = nullptr;   // backward dK/dV work items in launch order (-1 = idle)
   int32_t *kmask = nullptr;        // partial plans: n_tiles * tile_tokens/32 validity words
+  int32_t *swin = nullptr;         // SWA plans: heads*3 token windows
   void *block = nullptr;           // the single allocation holding all of the above
 };
 
@@ -104,6 +105,12 @@ struct sta_plan {
   bool partial = false;
   std::vector<int32_t> kmask;
 
+  // Token-wise sliding window attention (a comparison baseline): every query
+  // token has its own window of swin[3h..3h+2] tokens (clamped to the
+  // extents); tiles only group queries into work items.  No key-tile lists.
+  bool swa = false;
+  std::vector<int32_t> swin;
+
   mutable std::mutex mu;
   mutable std::map<int, sta::DeviceTables> dev;   // per HIP device ordinal
 };
@@ -115,6 +122,10 @@ namespace sta {
 // (the last tile of such an axis is partial; forward in natural layout only).
 sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[3],
                       const int *window, int head_dim, bool partial_ok, sta_plan **out);
+
+// Token-wise SWA plan (host only).  Defined in sta_plan.cpp.
+sta_status build_swa_plan(int batch, int heads, int T, int H, int W, const int tile[3],
+                          const int *window_tokens, int head_dim, sta_plan **out);
 
 // Releases device tables; defined in sta_api.hip (needs HIP).
 void release_device_tables(sta_plan *plan);

@@ -22,6 +22,10 @@ struct FwdArgs {
   int32_t max_nkv;         // longest key-tile list of any (head, query tile)
   float *lse;              // NULL, or [batch, heads, N] row log-sum-exp (natural log)
   const uint32_t *kmask;   // NULL (whole tiles), or per tile V/32 words of token validity
+  // Token-wise SWA plans only (swin == NULL otherwise): clamped token
+  // windows per head (heads*3), extents, query tile sizes, query tile grid.
+  const int32_t *swin;
+  int32_t T, H, W, tT, tH, tW, gH, gW;
 };
 
 // Launch the forward kernel.  variant: 0 generic, 1 384-query items.

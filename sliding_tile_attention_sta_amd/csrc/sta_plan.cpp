@@ -210,9 +210,91 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
   return STA_OK;
 }
 
+sta_status build_swa_plan(int batch, int heads, int T, int H, int W, const int tile[3],
+                          const int *window_tokens, int head_dim, sta_plan **out) {
+  if (!out || !tile || !window_tokens) return STA_ERR_ARG;
+  *out = nullptr;
+  if (batch < 1 || heads < 1 || T < 1 || H < 1 || W < 1) return STA_ERR_ARG;
+  for (int d = 0; d < 3; ++d)
+    if (tile[d] < 1) return STA_ERR_ARG;
+  for (int i = 0; i < heads * 3; ++i)
+    if (window_tokens[i] < 1) return STA_ERR_ARG;
+  const int ext[3] = {T, H, W};
+  for (int d = 0; d < 3; ++d)
+    if (ext[d] % tile[d] != 0) return STA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return STA_ERR_UNSUPPORTED;
+  const int64_t V64 = (int64_t)tile[0] * tile[1] * tile[2];
+  if (V64 % kKeyBlock != 0 || V64 > kMaxTileTokens) return STA_ERR_UNSUPPORTED;
+  const int64_t N64 = (int64_t)T * H * W;
+  if (N64 * batch * heads > (int64_t)INT32_MAX) return STA_ERR_UNSUPPORTED;
+  if (fwd_lds_bytes(head_dim, V64, 0) > kMaxLds) return STA_ERR_UNSUPPORTED;
+
+  sta_plan *p = new (std::nothrow) sta_plan();
+  if (!p) return STA_ERR_ALLOC;
+  try {
+    p->batch = batch; p->heads = heads; p->T = T; p->H = H; p->W = W; p->D = head_dim;
+    for (int d = 0; d < 3; ++d) { p->tile[d] = tile[d]; p->grid[d] = ext[d] / tile[d]; }
+    p->V = (int32_t)V64;
+    p->N = N64;
+    p->n_tiles = p->grid[0] * p->grid[1] * p->grid[2];
+    p->swa = true;
+    if (p->V % 384 == 0) {
+      p->variant = kTile384; p->qpi = 384;
+    } else {
+      p->variant = kGeneric; p->qpi = 32;
+    }
+    p->subs = p->V / p->qpi;
+    p->swin.resize((size_t)heads * 3);
+    p->win.resize((size_t)heads * 3);
+    for (int h = 0; h < heads; ++h)
+      for (int d = 0; d < 3; ++d) p->swin[h * 3 + d] = p->win[h * 3 + d] = std::min(window_tokens[h * 3 + d], ext[d]);
+    // Work per (head, query tile): rows (t, y) of the union of the tile's
+    // query windows times the 32-key runs covering its z range.
+    auto start = [](int x, int w, int e) { return std::min(std::max(x - (w - 1) / 2, 0), e - w); };
+    std::vector<int32_t> cost_off((size_t)heads * p->n_tiles + 1, 0);
+    const int nH = p->grid[1], nW = p->grid[2];
+    for (int h = 0; h < heads; ++h)
+      for (int qt = 0; qt < p->n_tiles; ++qt) {
+        const int c[3] = {qt / (nH * nW), (qt / nW) % nH, qt % nW};
+        int64_t span[3];
+        for (int d = 0; d < 3; ++d) {
+          const int w = p->swin[h * 3 + d];
+          const int lo = start(c[d] * tile[d], w, ext[d]);
+          const int hi = start(c[d] * tile[d] + tile[d] - 1, w, ext[d]) + w;
+          span[d] = hi - lo;
+        }
+        const int64_t steps = span[0] * span[1] * ((span[2] + kKeyBlock - 1) / kKeyBlock);
+        cost_off[(size_t)h * p->n_tiles + qt + 1] = cost_off[(size_t)h * p->n_tiles + qt] + (int32_t)steps;
+      }
+    p->kv_off.assign((size_t)heads * p->n_tiles + 1, 0);
+    p->q_off.assign((size_t)heads * p->n_tiles + 1, 0);
+    p->base_nat.resize(p->n_tiles);
+    for (int qt = 0; qt < p->n_tiles; ++qt) {
+      const int ct = qt / (nH * nW), cy = (qt / nW) % nH, cz = qt % nW;
+      p->base_nat[qt] = ((ct * tile[0]) * H + cy * tile[1]) * W + cz * tile[2];
+    }
+    p->off_nat.resize(p->V);
+    for (int j = 0; j < p->V; ++j) {
+      const int lt = j / (tile[1] * tile[2]), ly = (j / tile[2]) % tile[1], lz = j % tile[2];
+      p->off_nat[j] = (lt * H + ly) * W + lz;
+    }
+    p->sched = build_schedule(p, cost_off, p->subs);
+  } catch (const std::bad_alloc &) {
+    delete p;
+    return STA_ERR_ALLOC;
+  }
+  *out = p;
+  return STA_OK;
+}
+
 }  // namespace sta
 
 extern "C" {
+
+sta_status sta_swa_plan_create(int batch, int heads, int T, int H, int W, const int tile[3],
+                               const int *window_tokens, int head_dim, sta_plan **out) {
+  return sta::build_swa_plan(batch, heads, T, H, W, tile, window_tokens, head_dim, out);
+}
 
 sta_status sta_plan_create(int batch, int heads, int T, int H, int W, const int tile[3],
                            const int *window, int head_dim, sta_plan **out) {
@@ -244,6 +326,14 @@ sta_status sta_plan_get_info(const sta_plan *p, sta_plan_info *info) {
   info->tokens = p->N;
   info->pairs = p->pairs;
   info->flops = 4.0 * (double)p->V * (double)p->V * (double)p->D * (double)p->pairs * p->batch;
+  if (p->swa) {
+    // permitted (query, key) pairs only: every query sees prod(w') keys
+    double keys = 0.0;
+    for (int h = 0; h < p->heads; ++h)
+      keys += (double)p->swin[h * 3] * p->swin[h * 3 + 1] * p->swin[h * 3 + 2];
+    info->flops = 4.0 * (double)p->N * keys * p->D * p->batch;
+  }
+  info->swa = p->swa ? 1 : 0;
   info->work_items = (int64_t)p->sched.size();
   info->queries_per_item = p->qpi;
   info->kernel_variant = p->variant;
@@ -258,7 +348,7 @@ sta_status sta_plan_get_info(const sta_plan *p, sta_plan_info *info) {
 
 sta_status sta_plan_perm(const sta_plan *p, int32_t *perm, int64_t cap) {
   if (!p || !perm || cap < p->N) return STA_ERR_ARG;
-  if (p->partial) return STA_ERR_UNSUPPORTED;
+  if (p->partial || p->swa) return STA_ERR_UNSUPPORTED;
   for (int qt = 0; qt < p->n_tiles; ++qt)
     for (int j = 0; j < p->V; ++j) perm[(int64_t)qt * p->V + j] = p->base_nat[qt] + p->off_nat[j];
   return STA_OK;

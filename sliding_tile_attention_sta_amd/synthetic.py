@@ -86,6 +86,18 @@ WORKLOADS = {
     "partial-small": Workload("partial-small", 9, (5, 13, 11), (2, 4, 4), ((3, 3, 3), (1, 2, 5)), 64,
                               "f32", description="5x13x11 latent, tile 2x4x4 (partial on every "
                                                  "axis), windows 3x3x3 and 1x2x5, 2 heads, d64, fp32"),
+    # Token-wise sliding window attention (the baseline STA is contrasted
+    # with): windows in TOKENS; tiles only group queries into work items.
+    # 18x24x24 tokens = the key count of STA's 3x3x3 window of 6x8x8 tiles.
+    "swa-720p": Workload("swa-720p", 10, (30, 48, 80), (6, 8, 8), ((18, 24, 24),) * 24, 128, "bf16",
+                         description="token-wise SWA: 30x48x80 latent, window 18x24x24 tokens "
+                                     "(10368 keys per query), 24 heads, d128, bf16"),
+    "swa-small": Workload("swa-small", 11, (12, 24, 24), (6, 8, 8), ((9, 12, 12), (5, 24, 7)) * 2, 128,
+                          "bf16", description="token-wise SWA: 12x24x24 latent, windows 9x12x12 and "
+                                              "5x24x7 tokens, 4 heads, d128, bf16"),
+    "swa-tiny": Workload("swa-tiny", 12, (6, 16, 16), (2, 4, 4), ((5, 7, 9), (3, 3, 3)), 64, "f32",
+                         description="token-wise SWA: 6x16x16 latent, windows 5x7x9 and 3x3x3 tokens, "
+                                     "2 heads, d64, fp32"),
     # 2D STA (an image latent: T = 1, tiles of one frame)
     "2d": Workload("2d", 6, (1, 96, 96), (1, 16, 24), ((1, 3, 3),) * 8, 128, "bf16",
                    description="2D: 96x96 latent, tile 16x24 (384 tokens), window 3x3 tiles, "

@@ -346,3 +346,29 @@ def test_partial_plan_geometry_and_unsupported_paths():
     # whole tiles through the flag: an ordinary plan
     q2 = api.Plan(1, 2, (30, 48, 80), tile, [window], 128, partial_tiles=True)
     assert q2.info.partial_tiles == 0 and q2.info.bwd_supported == 1
+
+
+# ---------------------------------------------------------------------------
+# Token-wise SWA plans
+# ---------------------------------------------------------------------------
+
+def test_swa_plan_info_and_unsupported_paths():
+    p = api.Plan(1, 2, (30, 48, 80), (6, 8, 8), [(18, 24, 24), (100, 5, 3)], 128, token_windows=True)
+    info = p.info
+    assert info.swa == 1 and info.bwd_supported == 0 and info.kernel_variant == 1
+    # permitted pairs only: every query sees prod(min(w, extent)) keys
+    assert info.flops == 4.0 * 115200 * (18 * 24 * 24 + 30 * 5 * 3) * 128
+    s = p.schedule().numpy()
+    assert sorted(s[s >= 0].tolist()) == list(range(2 * 300))
+    lib = L.lib()
+    P = ctypes.c_void_p
+    q, k, v, o = P(1 << 40), P(2 << 40), P(3 << 40), P(4 << 40)
+    assert lib.sta_forward_plan(p.handle, q, k, v, o, 0.125, 0, 1, L.STA_LAYOUT_TILE_MAJOR, None) == L.STA_ERR_UNSUPPORTED
+    assert lib.sta_tile_reorder(p.handle, q, o, 0, None) == L.STA_ERR_UNSUPPORTED
+    buf = (ctypes.c_int32 * 115200)()
+    assert lib.sta_plan_perm(p.handle, buf, 115200) == L.STA_ERR_UNSUPPORTED
+    h = ctypes.c_void_p()
+    assert lib.sta_swa_plan_create(1, 1, 30, 47, 80, _ints([6, 8, 8]), _ints([3, 3, 3]), 128,
+                                   ctypes.byref(h)) == L.STA_ERR_SHAPE
+    assert lib.sta_swa_plan_create(1, 1, 30, 48, 80, _ints([6, 8, 8]), _ints([3, 0, 3]), 128,
+                                   ctypes.byref(h)) == L.STA_ERR_ARG
