@@ -106,6 +106,97 @@ def cpu_baseline(w, q, k, v, budget_s=12.0):
     }
 
 
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def _timed_tiles(w, heads_tiles, fn, flops_per_tile, budget_s):
+    """Run fn(head, tile) over (head, tile) pairs until budget_s seconds of
+    CPU work; returns (tiles done, FLOPs, seconds, last head)."""
+    done, flops, t_used, last = 0, 0.0, 0.0, 0
+    for h, c in heads_tiles:
+        t0 = time.perf_counter()
+        fn(h, c)
+        t_used += time.perf_counter() - t0
+        done += 1
+        flops += flops_per_tile(h)
+        last = h
+        if t_used >= budget_s:
+            break
+    return done, flops, t_used, last
+
+
+def cpu_baseline_bwd(w, q, k, v, g, budget_s=10.0):
+    """The backward oracle on a bounded sample: dq and lse of query tiles of
+    head 0, 1, ... (each call forms every gradient product of its tile's
+    window pairs: 2.5x the forward's FLOPs per pair, counted as such)."""
+    from oracle import sta_oracle as O
+    from oracle import sta_oracle_bwd as OB
+    from sliding_tile_attention_sta_amd.synthetic import sample_query_tiles
+    grid = O.tile_grid(w.video, w.tile)
+    V = w.tile[0] * w.tile[1] * w.tile[2]
+    cache = {}
+
+    def heads_tiles():
+        for h in range(w.heads):
+            for c in sample_query_tiles(w, h):
+                yield h, c
+
+    def fn(h, c):
+        if h not in cache:
+            cache.clear()
+            cache[h] = [x[:, h:h + 1].float().cpu().numpy() for x in (q, k, v, g)]
+        OB.sta_backward_query_tiles(*cache[h], w.tile, w.windows[h], 0, [c], scale=w.scale)
+
+    def fl(h):
+        we = O.effective_window(w.windows[h], grid)
+        return 2.5 * 4.0 * V * V * w.head_dim * we[0] * we[1] * we[2]
+
+    done, flops, t_used, last = _timed_tiles(w, heads_tiles(), fn, fl, budget_s)
+    full_s = t_used * 2.5 * O.sta_flops(w.video, w.tile, w.windows, w.head_dim, w.batch) / flops
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"{done} query tiles (heads 0..{last}) of the {w.name} workload through the "
+                      f"backward oracle, float64 numpy, {t_used:.1f} s; a full backward extrapolates "
+                      f"to {full_s:.0f} s",
+            "seconds": t_used, "cpu_model": _cpu_model()}
+
+
+def cpu_baseline_swa(w, q, k, v, toks, budget_s=10.0):
+    """The token-wise SWA oracle on a bounded sample of query tiles."""
+    from oracle import sta_oracle_swa as OS
+    from sliding_tile_attention_sta_amd.synthetic import sample_query_tiles
+    V = w.tile[0] * w.tile[1] * w.tile[2]
+    cache = {}
+
+    def heads_tiles():
+        for h in range(w.heads):
+            for c in sample_query_tiles(w, h):
+                yield h, c
+
+    def fn(h, c):
+        if h not in cache:
+            cache.clear()
+            cache[h] = [x[:, h:h + 1].float().cpu().numpy() for x in (q, k, v)]
+        OS.swa_forward_query_tiles(*cache[h], w.tile, toks[h], 0, [c], scale=w.scale)
+
+    def fl(h):
+        keys = 1
+        for a, e in zip(toks[h], w.video):
+            keys *= min(a, e)
+        return 4.0 * V * keys * w.head_dim
+
+    done, flops, t_used, last = _timed_tiles(w, heads_tiles(), fn, fl, budget_s)
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s (permitted pairs)", "cores": _threads(),
+            "kind": "oracle",
+            "sample": f"{done} query tiles (heads 0..{last}) of the {w.name} workload through the "
+                      f"token-wise SWA oracle, float64 numpy, {t_used:.1f} s",
+            "seconds": t_used, "cpu_model": _cpu_model()}
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -140,7 +231,9 @@ def backward(args, w, plan, q, k, v, stream):
     # The two kernels execute seven (dQ recomputes Q K^T and dO V^T).
     flops = 2.5 * fwd_flops
     tflops = flops / (ms * 1e-3) / 1e12
+    cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(w, q, k, v, g)
     return {
+        "cpu_baseline": cpu,
         "metric": "STA bwd ms + achieved TFLOP/s (algorithmic, 2.5x forward FLOPs)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
@@ -189,6 +282,34 @@ def search(args, w, stream):
     flops = per_pair * pairs
     tau = 0.1
     windows = api.window_select(err, cands, grid, tau)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's per-query-tile STA forward over the candidates for
+        # sampled tiles of head 0, then 1, ..., until ~10 s; its FLOP rate
+        # extrapolates the oracle's time for the whole sweep
+        from oracle import sta_oracle as O
+        from sliding_tile_attention_sta_amd.synthetic import sample_query_tiles
+        qs, ks, vs = None, None, None
+        done, fl, t_used, hh = 0, 0.0, 0.0, 0
+        while t_used < 10.0 and hh < w.heads:
+            qs, ks, vs = (x[:, hh:hh + 1].float().cpu().numpy() for x in (q, k, v))
+            for c in sample_query_tiles(w, hh, count=4)[:4]:
+                for win in cands:
+                    t0 = time.perf_counter()
+                    O.sta_forward_query_tiles(qs, ks, vs, w.tile, win, 0, [c], scale=w.scale)
+                    t_used += time.perf_counter() - t0
+                    fl += 4.0 * V * V * w.head_dim * (min(win[0], grid[0]) * min(win[1], grid[1]) *
+                                                     min(win[2], grid[2]))
+                    done += 1
+                if t_used >= 10.0:
+                    break
+            hh += 1
+        rate = fl / t_used
+        cpu = {"value": round(flops / rate, 1), "unit": "s per sweep (extrapolated)", "cores": _threads(),
+               "kind": "oracle",
+               "sample": f"{done} (query tile, candidate) forwards of heads 0..{hh - 1} through the "
+                         f"oracle, float64 numpy, {t_used:.1f} s, {rate / 1e12:.3f} TFLOP/s",
+               "seconds": t_used, "cpu_model": _cpu_model()}
     kept = sum(a * b * c for a, b, c in windows) / (len(windows) * n_tiles)
     return {
         "metric": "STA per-head window search: seconds per candidate sweep",
@@ -198,6 +319,7 @@ def search(args, w, stream):
         "config": {"workload": w.name + "-locality", "video": list(w.video), "tile": list(w.tile),
                    "heads": w.heads, "head_dim": w.head_dim, "lengths": lengths,
                    "candidates": len(cands), "threshold": tau},
+        "cpu_baseline": cpu,
         "forward_tflops": round(flops / sec / 1e12, 1),
         "chosen_windows": windows,
         "attended_fraction_of_dense": round(kept, 4),
@@ -242,7 +364,9 @@ def swa(args, w, plan, q, k, v, stream):
                     blocks += a * b * ((c + 31) // 32)
     executed = 4.0 * blocks * 32 * V * w.head_dim * w.batch
     fl_swa = splan.flops
+    cpu = None if args.no_cpu_baseline else cpu_baseline_swa(w, q, k, v, toks)
     return {
+        "cpu_baseline": cpu,
         "metric": "token-wise SWA fwd ms vs STA fwd ms, same keys per query",
         "value": round(ms_swa / ms_sta, 3), "unit": "SWA time / STA time", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_swa, 4),
