@@ -242,7 +242,7 @@ def backward(args, w, plan, q, k, v, stream):
                    "windows": sorted({tuple(x) for x in w.windows}), "heads": w.heads,
                    "head_dim": w.head_dim, "batch": w.batch, "layout": "natural",
                    "in_dtype": "bf16", "grad_dtype": "f32",
-                   "products": "fp16 MFMA, fp32 accumulate", "flops_per_step": flops,
+                   "products": "fp16 MFMA (bf16 for the dQ kernel's dO V^T), fp32 accumulate", "flops_per_step": flops,
                    "executed_flops_per_step": 3.5 * fwd_flops},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,

@@ -27,16 +27,20 @@
 //     the keys' K and V in VGPRs, then dV^T += dO^T P and dK^T += Q^T dS with
 //     dO^T and Q^T read transposed from LDS.
 //
-// Every product runs on v_mfma_f32_16x16x32_f16 with fp32 accumulation.
+// The products run on v_mfma_f32_16x16x32_f16 with fp32 accumulation.
 // P and dS are rounded to fp16 (11 significant bits against bf16's 8); Q and
 // K are the forward's bf16 values (fp32 inputs rounded to bf16 first, so
 // that the scores match the ones the forward's lse was taken over), widened
 // to fp16, which is exact inside the fp16 range; V and dO are converted to
-// fp16 (exact for bf16 values inside the range, nearest-even for fp32).
+// fp16 (exact for bf16 values inside the range, nearest-even for fp32).  One
+// exception: with bf16 inputs the dQ kernel's dP^T = V dO^T takes V and dO
+// as they are on v_mfma_f32_16x16x32_bf16 (the same exact products, without
+// the per-step conversion of V).
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "sta_device.h"
 #include "sta_internal.h"
@@ -61,6 +65,15 @@ __device__ __forceinline__ uint4 score_f16(const Raw8<F32> &r) {
 }
 
 __device__ __forceinline__ f16x8 lds_f16x8(const char *p) { return *reinterpret_cast<const f16x8 *>(p); }
+__device__ __forceinline__ bf16x8 lds_bf16x8(const char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// V and dO for the dQ kernel's dP^T: bf16 chunks as they are, fp32 chunks
+// converted to fp16.
+template <bool F32>
+__device__ __forceinline__ uint4 dp_operand(const Raw8<F32> &r) {
+  if constexpr (F32) return as_f16<true>(r);
+  else return r.x;
+}
 
 // Transposed 16x16x32 operand from a row-major fp16 [32][*] LDS block: lane
 // (g, l16) receives column col0 + l16 of rows 4g..4g+3 (slots 0..3) and
@@ -148,8 +161,12 @@ __device__ __forceinline__ Item decode(int item, const BwdArgs &a) {
 template <int D, int NW, bool F32IN>
 // Two waves per SIMD: without the hint the allocator parks the Q and dO
 // fragments in AGPRs and copies them back every step (about 100 extra VALU
-// instructions per step).
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sta_bwd_dq_kernel(BwdArgs a) {
+// instructions per step).  Except for one wave with D = 128 (tile volumes
+// that are not a multiple of 128): it stages 8 chunks of K and of V per
+// step, which does not fit in 256 VGPRs, and the AGPRs are the place to
+// spill to (with the hint it spilled to scratch).
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bwd_dq_kernel(BwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QPI = 32 * NW;
   constexpr int STR = bwd_stride(D);
@@ -187,7 +204,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __syncthreads();
 
   // Q and dO of the wave's 32 queries (B operands; lane: query 16j + l16).
-  f16x8 qf[2][DC], gf[2][DC];
+  using DpT = typename std::conditional<F32IN, f16x8, bf16x8>::type;
+  f16x8 qf[2][DC];
+  DpT gf[2][DC];
   float lse2[2], dl[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -196,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int c = 0; c < DC; ++c) {
       const size_t e = (size_t)row * D + 32 * c + 8 * g;
       qf[j][c] = __builtin_bit_cast(f16x8, score_f16<F32IN>(load_raw<F32IN>(qg + e * EB)));
-      gf[j][c] = __builtin_bit_cast(f16x8, as_f16<F32IN>(load_raw<F32IN>(gg + e * EB)));
+      gf[j][c] = __builtin_bit_cast(DpT, dp_operand<F32IN>(load_raw<F32IN>(gg + e * EB)));
     }
     lse2[j] = a.lse[plane + row] * kLog2e;
     dl[j] = a.delta[plane + row];
@@ -224,7 +243,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if (CHUNKS < NT && c >= CHUNKS) break;
       const int o = (c / (D / 8)) * STR + (c % (D / 8)) * 16;
       *reinterpret_cast<uint4 *>(ks + o) = score_f16<F32IN>(rk[i]);
-      *reinterpret_cast<uint4 *>(vs + o) = as_f16<F32IN>(rv[i]);
+      *reinterpret_cast<uint4 *>(vs + o) = dp_operand<F32IN>(rv[i]);
     }
   };
 
@@ -257,11 +276,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         const int o = (kb * 16 + l16) * STR + (32 * c + 8 * g) * 2;
-        const f16x8 ka = lds_f16x8(ks + o), va = lds_f16x8(vs + o);
+        const f16x8 ka = lds_f16x8(ks + o);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          st[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[j][c], st[kb][j], 0, 0, 0);
-          dp[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, gf[j][c], dp[kb][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) st[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[j][c], st[kb][j], 0, 0, 0);
+        if constexpr (F32IN) {
+          const f16x8 va = lds_f16x8(vs + o);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) dp[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, gf[j][c], dp[kb][j], 0, 0, 0);
+        } else {
+          const bf16x8 va = lds_bf16x8(vs + o);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) dp[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, gf[j][c], dp[kb][j], 0, 0, 0);
         }
       }
     // Next key block's loads, issued once the score accumulators are formed.

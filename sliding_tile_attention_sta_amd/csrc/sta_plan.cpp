@@ -171,8 +171,12 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
     }
     p->sched = build_schedule(p, p->kv_off, p->subs);
 
-    // Backward: the inverse of the key-tile lists (query tiles, ascending),
-    // per head, and the two backward schedules.
+    // Backward: the inverse of the key-tile lists (query tiles whose window
+    // holds the key tile), per head, and the two backward schedules.  Launch
+    // order inside a list: by (a mod wT, b mod wH, c mod wW) as for the key
+    // tiles, ties in raster order.  Away from the borders a key tile is seen
+    // by w consecutive query tiles per axis, so key tiles that share query
+    // tiles visit them at the same step.
     p->q_off.assign((size_t)heads * p->n_tiles + 1, 0);
     {
       std::vector<std::vector<int32_t>> inv(p->n_tiles);
@@ -182,7 +186,14 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
           const size_t i = (size_t)h * p->n_tiles + qt;
           for (int32_t e = p->kv_off[i]; e < p->kv_off[i + 1]; ++e) inv[p->kv_idx[e]].push_back(qt);
         }
+        const int *w = &p->win[h * 3];
+        auto residue = [&](int32_t t) {
+          const int ct = t / (nH * nW), cy = (t / nW) % nH, cz = t % nW;
+          return ((ct % w[0]) * w[1] + cy % w[1]) * w[2] + cz % w[2];
+        };
         for (int kt = 0; kt < p->n_tiles; ++kt) {
+          std::stable_sort(inv[kt].begin(), inv[kt].end(),
+                           [&](int32_t x, int32_t y) { return residue(x) < residue(y); });
           p->q_idx.insert(p->q_idx.end(), inv[kt].begin(), inv[kt].end());
           p->q_off[(size_t)h * p->n_tiles + kt + 1] = (int32_t)p->q_idx.size();
           p->max_nq = std::max(p->max_nq, (int32_t)inv[kt].size());
@@ -372,10 +383,12 @@ sta_status sta_plan_q_tiles(const sta_plan *p, int head, int kv_tile, int32_t *o
   if (!p || !count || head < 0 || head >= p->heads || kv_tile < 0 || kv_tile >= p->n_tiles)
     return STA_ERR_ARG;
   const size_t i = (size_t)head * p->n_tiles + kv_tile;
-  const int n = p->q_off[i + 1] - p->q_off[i];
+  std::vector<int32_t> list(p->q_idx.begin() + p->q_off[i], p->q_idx.begin() + p->q_off[i + 1]);
+  std::sort(list.begin(), list.end());
+  const int n = (int)list.size();
   *count = n;
   if (!out && cap > 0) return STA_ERR_ARG;
-  for (int j = 0; j < cap && j < n; ++j) out[j] = p->q_idx[p->q_off[i] + j];
+  for (int j = 0; j < cap && j < n; ++j) out[j] = list[j];
   return n > cap ? STA_ERR_ARG : STA_OK;
 }
 

@@ -63,6 +63,14 @@ _MIXED = ((1, 1, 1), (3, 3, 3), (3, 5, 5), (5, 6, 10))
 WORKLOADS = {
     "tiny": Workload("tiny", 1, (6, 16, 16), (2, 4, 4), ((3, 3, 3),) * 2, 64, "f32",
                      description="6x16x16 latent, tile 2x4x4, window 3x3x3, 2 heads, d64, fp32"),
+    # head_dim 128 with 64-token tiles: the kernels' one-wave (generic)
+    # variants at the larger head size.
+    "generic-d128": Workload("generic-d128", 13, (8, 16, 16), (2, 4, 8), ((3, 3, 3), (1, 4, 2)), 128,
+                             "bf16", description="8x16x16 latent, tile 2x4x8 (64 tokens), windows "
+                                                 "3x3x3 and 1x4x2, 2 heads, d128, bf16"),
+    "generic-d128-f32": Workload("generic-d128-f32", 14, (8, 16, 16), (2, 4, 8), ((3, 3, 3), (2, 1, 2)),
+                                 128, "f32", description="8x16x16 latent, tile 2x4x8 (64 tokens), "
+                                                         "windows 3x3x3 and 2x1x2, 2 heads, d128, fp32"),
     "small": Workload("small", 2, (12, 24, 24), (6, 8, 8), ((3, 3, 3),) * 8, 128, "bf16",
                       description="12x24x24 latent, tile 6x8x8, window 3x3x3 (covers the grid), "
                                   "8 heads, d128, bf16"),

@@ -91,13 +91,17 @@ def consumed(q, k, v, g):
 def _all_tokens(w, heads, grad_dtype=torch.float32):
     q, k, v = make_qkv(w)
     g = make_grad_out(w)
-    _, _, lse, dq, dk, dv = run_bwd(w, q.cuda(), k.cuda(), v.cuda(), g.cuda(), grad_dtype=grad_dtype)
+    _, out, lse, dq, dk, dv = run_bwd(w, q.cuda(), k.cuda(), v.cuda(), g.cuda(), grad_dtype=grad_dtype)
     q, k, v, g = consumed(q, k, v, g)
     for h in heads:
         sl = slice(h, h + 1)
         ref = OB.sta_backward_explicit(*(flat(x, w)[:, sl].double().numpy() for x in (q, k, v, g)),
                                        w.video, w.tile, [w.windows[h]], scale=w.scale)
         say(f" head {h}")
+        # the forward's own bound (absolute): max 2e-2, mean 2e-3
+        do = np.abs(flat(out, w)[:, sl].cpu().numpy().astype(np.float64) - ref["o"])
+        say(f"  o: max {do.max():.2e} mean {do.mean():.2e}")
+        assert do.max() <= 2e-2 and do.mean() <= 2e-3
         check_lse(lse[:, sl].cpu().numpy(), ref["lse"])
         for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
             check_grad(name, flat(t, w)[:, sl].float().cpu().numpy(), ref[name])
@@ -106,6 +110,13 @@ def _all_tokens(w, heads, grad_dtype=torch.float32):
 def test_tiny_all_tokens():
     w = WORKLOADS["tiny"]
     say("case tiny backward: 6x16x16 tile 2x4x4 w333 2 heads d64 fp32")
+    _all_tokens(w, range(w.heads))
+
+
+@pytest.mark.parametrize("name", ["generic-d128", "generic-d128-f32"])
+def test_generic_d128_all_tokens(name):
+    w = WORKLOADS[name]
+    say(f"case {name} backward: 8x16x16 tile 2x4x8 (one-wave kernels) 2 heads d128 {w.dtype}")
     _all_tokens(w, range(w.heads))
 
 
