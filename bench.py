@@ -66,6 +66,41 @@ def timed(fn, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def per_call_ms(fn, calls, stream):
+    """Each call bracketed by its own pair of events (after the timed
+    region): median, min and max milliseconds per call."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    return {"calls": calls, "median": round(t[len(t) // 2], 4), "min": round(t[0], 4), "max": round(t[-1], 4)}
+
+
+def sdpa_dense(q, k, v, scale, stream, ms_sta):
+    """torch's scaled_dot_product_attention on the whole sequence (dense),
+    restricted to its flash backend so that it never takes the math path;
+    a library kernel, reported for context."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    B, Hh = q.shape[0], q.shape[1]
+    qs, ks, vs = (x.reshape(B, Hh, -1, x.shape[-1]) for x in (q, k, v))
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            f = lambda: torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, scale=scale)
+            ms = timed(f, 3, 1, stream)
+    except RuntimeError as e:
+        return {"skipped": str(e).splitlines()[0][:160]}
+    n = qs.shape[2]
+    flops = 4.0 * B * Hh * n * n * qs.shape[-1]
+    return {"backend": "torch SDPA, flash backend (library kernel)", "ms": round(ms, 3),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "sta_speedup": round(ms / ms_sta, 2)}
+
+
 def cpu_baseline(w, q, k, v, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample: query tiles of head 0
     (then 1, ...) until about budget_s seconds of CPU work."""
@@ -475,6 +510,14 @@ def main():
         "roofline": roofline,
     }
 
+    result["per_call_ms"] = per_call_ms(step, args.steps, stream)
+    if not args.no_context:
+        out_b = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        ms_b = timed(lambda: api.sta_forward_plan(plan, q, k, v, out=out_b, scale=w.scale, layout="natural",
+                                                  stream=stream), max(3, args.steps // 2), 1, stream)
+        result["bf16_out"] = {"ms": round(ms_b, 4), "tflops": round(flops / (ms_b * 1e-3) / 1e12, 2)}
+        del out_b
+
     if not args.no_context and not partial:
         # explicit reorder -> tile-major forward -> unreorder
         qt, kt, vt = (api.sta_tile_reorder(plan, x) for x in (q, k, v))
@@ -512,6 +555,8 @@ def main():
         result["dense_context"] = {"ms": round(ms_d, 3),
                                    "tflops": round(dplan.flops / (ms_d * 1e-3) / 1e12, 2),
                                    "sta_speedup": round(ms_d / ms, 2)}
+        if w.dtype == "bf16":
+            result["sdpa_dense_context"] = sdpa_dense(q, k, v, w.scale, stream, ms)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v)
