@@ -496,10 +496,15 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     stash_v(cv, s & 1);
     __syncthreads();
   };
-  for (int s = 0; s < nsteps; s += 2) {
+  // An odd last step runs after the loop: with it inside (a conditional
+  // second step), the path that skips it returns to the loop head with the
+  // first step's loads still outstanding, and the compiler's wait for them
+  // at the head then also retired every iteration's newest loads.
+  for (int s = 0; s + 1 < nsteps; s += 2) {
     step(s, rk, rv, rk2, rv2);
-    if (s + 1 < nsteps) step(s + 1, rk2, rv2, rk, rv);
+    step(s + 1, rk2, rv2, rk, rv);
   }
+  if (nsteps & 1) step(nsteps - 1, rk, rv, rk2, rv2);
   if (!grp_a) softmax();
   pvmm((nsteps - 1) & 1);
 
