@@ -243,6 +243,22 @@ def _cpu_model():
     return "unknown"
 
 
+def _measured_traffic(path, source, workload, key):
+    """HBM bytes from a committed rocprofv3 counter summary, used only while
+    the kernel source hashes to the one measured (else None)."""
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sliding_tile_attention_sta_amd", "csrc", source)
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") == workload and t.get("kernel_source_sha256") == digest:
+        return t.get(key)
+    return None
+
+
 def backward(args, w, plan, q, k, v, stream):
     """One step = the STA backward call (delta, dQ and dK/dV kernels) for
     the forward's output and row log-sum-exp, computed once beforehand."""
@@ -267,6 +283,8 @@ def backward(args, w, plan, q, k, v, stream):
     flops = 2.5 * fwd_flops
     tflops = flops / (ms * 1e-3) / 1e12
     cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(w, q, k, v, g)
+    traffic = _measured_traffic(os.path.join(os.path.dirname(args.traffic_json), "traffic_bwd.json"),
+                                "sta_backward.hip", w.name, "bytes_per_call")
     return {
         "cpu_baseline": cpu,
         "metric": "STA bwd ms + achieved TFLOP/s (algorithmic, 2.5x forward FLOPs)",
@@ -280,7 +298,8 @@ def backward(args, w, plan, q, k, v, stream):
                    "products": "fp16 MFMA (bf16 for the dQ kernel's dO V^T), fp32 accumulate", "flops_per_step": flops,
                    "executed_flops_per_step": 3.5 * fwd_flops},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per call (HBM, FETCH_SIZE + WRITE_SIZE of the three kernels, copy-calibrated)",
                      "kernel": "whole backward call (delta + dQ + dK/dV)"},
     }
 
@@ -470,19 +489,7 @@ def main():
     # per-launch kernel duration is the event time per step.
     # HBM traffic per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     # measurement, used only while the kernel source is the one measured.
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            with open(args.traffic_json) as f:
-                t = json.load(f)
-            src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sliding_tile_attention_sta_amd",
-                               "csrc", "sta_forward.hip")
-            with open(src, "rb") as f:
-                digest = hashlib.sha256(f.read()).hexdigest()
-            if t.get("workload") == w.name and t.get("kernel_source_sha256") == digest:
-                traffic = t.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+    traffic = _measured_traffic(args.traffic_json, "sta_forward.hip", w.name, "bytes_per_launch")
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "traffic_unit": "bytes per launch (HBM, FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
