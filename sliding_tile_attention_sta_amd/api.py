@@ -7,6 +7,7 @@ in its own HIP kernels.  PyTorch provides device memory and the stream.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 from typing import Sequence
@@ -45,6 +46,14 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on(stream):
+    """Buffers allocated for a call belong to the stream the call runs on:
+    the caching allocator then hands a freed buffer (the backward's delta)
+    only to later work on that stream, never to other streams while the
+    call's kernels still use it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 class Plan:
@@ -148,7 +157,8 @@ def _check_tensor(x: torch.Tensor, plan: Plan, name: str):
 def _reorder(fn, plan: Plan, x: torch.Tensor, out, stream):
     _check_tensor(x, plan, "x")
     if out is None:
-        out = torch.empty_like(x)
+        with _on(stream):
+            out = torch.empty_like(x)
     _check_tensor(out, plan, "out")
     if out.dtype != x.dtype:
         raise ValueError("out must have the input's dtype")
@@ -189,7 +199,8 @@ def sta_forward_plan(plan: Plan, q, k, v, out=None, scale: float | None = None,
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        with _on(stream):
+            out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     _check_tensor(out, plan, "out")
     if scale is None:
         scale = 1.0 / math.sqrt(plan.info.head_dim)
@@ -200,7 +211,8 @@ def sta_forward_plan(plan: Plan, q, k, v, out=None, scale: float | None = None,
         return out
     if lse is True:
         i = plan.info
-        lse = torch.empty((i.batch, i.heads, i.tokens), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            lse = torch.empty((i.batch, i.heads, i.tokens), dtype=torch.float32, device=q.device)
     _check_rows(lse, plan, "lse")
     L.check(L.lib().sta_forward_plan_lse(*args, _ptr(lse), *tail), "sta_forward_plan_lse")
     return out, lse
@@ -218,12 +230,14 @@ def sta_backward_plan(plan: Plan, q, k, v, out, dout, lse, scale: float | None =
     _check_rows(lse, plan, "lse")
     i = plan.info
     if delta is None:
-        delta = torch.empty((i.batch, i.heads, i.tokens), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            delta = torch.empty((i.batch, i.heads, i.tokens), dtype=torch.float32, device=q.device)
     _check_rows(delta, plan, "delta")
     grads = []
     for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
         if g is None:
-            g = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+            with _on(stream):
+                g = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
         _check_tensor(g, plan, name)
         grads.append(g)
     if not (grads[0].dtype == grads[1].dtype == grads[2].dtype):
@@ -282,7 +296,8 @@ def sta_forward(q, k, v, tile, windows, scale: float | None = None, out=None,
         if not x.is_cuda or not x.is_contiguous() or x.dtype not in _DTYPES or x.shape != q.shape:
             raise ValueError(f"{name}: contiguous CUDA bf16/fp32 tensor shaped like q required")
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        with _on(stream):
+            out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     st = L.lib().sta_forward(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
