@@ -223,27 +223,33 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
 
   const int spt = a.V / TB;
   const int nsteps = nl * spt;
-  Raw8<F32IN> rk[CPT], rv[CPT];
-  auto fetch = [&](int s) {
+  // K/V chunks pass through two register buffers: block s+2 is loaded at
+  // the start of step s into one while the other (block s+1, loaded a step
+  // earlier) is written to LDS at its end, so every block's loads have a
+  // whole step to arrive.  Loads past the last block re-read it, into a
+  // stage nobody reads again.
+  Raw8<F32IN> rka[CPT], rva[CPT], rkb[CPT], rvb[CPT];
+  auto fetch = [&](int s, Raw8<F32IN>(&dk)[CPT], Raw8<F32IN>(&dv)[CPT]) {
+    if (s > nsteps - 1) s = nsteps - 1;
     const int tb = lb_l[s / spt], u = s % spt;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (CHUNKS < NT && c >= CHUNKS) break;
       const size_t e = (size_t)(tb + off_l[u * TB + c / (D / 8)]) * D + (c % (D / 8)) * 8;
-      rk[i] = load_raw<F32IN>(kg + e * EB);
-      rv[i] = load_raw<F32IN>(vg + e * EB);
+      dk[i] = load_raw<F32IN>(kg + e * EB);
+      dv[i] = load_raw<F32IN>(vg + e * EB);
     }
   };
-  auto stash = [&](int stage) {
+  auto stash = [&](const Raw8<F32IN>(&sk)[CPT], const Raw8<F32IN>(&sv)[CPT], int stage) {
     char *ks = smem + stage * ST, *vs = smem + (2 + stage) * ST;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (CHUNKS < NT && c >= CHUNKS) break;
       const int o = (c / (D / 8)) * STR + (c % (D / 8)) * 16;
-      *reinterpret_cast<uint4 *>(ks + o) = score_f16<F32IN>(rk[i]);
-      *reinterpret_cast<uint4 *>(vs + o) = dp_operand<F32IN>(rv[i]);
+      *reinterpret_cast<uint4 *>(ks + o) = score_f16<F32IN>(sk[i]);
+      *reinterpret_cast<uint4 *>(vs + o) = dp_operand<F32IN>(sv[i]);
     }
   };
 
@@ -256,11 +262,14 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
   const int trow = 4 * g + (l16 >> 2), tcol = 4 * (l16 & 3);
 
   if (nsteps > 0) {
-    fetch(0);
-    stash(0);
+    fetch(0, rka, rva);
+    stash(rka, rva, 0);
+    fetch(1, rka, rva);
   }
   __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
+  auto step = [&](int s, const Raw8<F32IN>(&ck)[CPT], const Raw8<F32IN>(&cv)[CPT], Raw8<F32IN>(&nk)[CPT],
+                  Raw8<F32IN>(&nv)[CPT]) {
+    fetch(s + 2, nk, nv);
     const char *ks = smem + (s & 1) * ST, *vs = smem + (2 + (s & 1)) * ST;
     // S^T = K Q^T, dP^T = V dO^T; lane: query 16j + l16, keys 16kb + 4g + r.
     f32x4 st[2][2], dp[2][2];
@@ -289,9 +298,6 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
           for (int j = 0; j < 2; ++j) dp[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, gf[j][c], dp[kb][j], 0, 0, 0);
         }
       }
-    // Next key block's loads, issued once the score accumulators are formed.
-    const bool more = s + 1 < nsteps;
-    if (more) fetch(s + 1);
     // dS^T in fp16, slots: keys 4g + r (kb 0) and 16 + 4g + r (kb 1).
     f16x8 dsf[2];
 #pragma unroll
@@ -310,8 +316,18 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kt, dsf[j], acc[b][j], 0, 0, 0);
     }
-    if (more) stash((s + 1) & 1);
+    stash(ck, cv, (s + 1) & 1);
     __syncthreads();
+  };
+  // Two steps per iteration (the buffers alternate); an odd last step runs
+  // after the loop, so that no path back to the loop head leaves loads
+  // outstanding in the buffer the next iteration loads into.
+  if (nsteps > 0) {
+    for (int s = 0; s + 1 < nsteps; s += 2) {
+      step(s, rka, rva, rkb, rvb);
+      step(s + 1, rkb, rvb, rka, rva);
+    }
+    if (nsteps & 1) step(nsteps - 1, rka, rva, rkb, rvb);
   }
 
   // dQ = scale * acc; lane: query 16j + l16, d = 16b + 4g + r.
