@@ -1,14 +1,16 @@
 """Forward and backward parity on seeded random small plans (needs MI355X).
 
-Each case draws a tile shape (volumes 32 to 384, so both forward variants
-and every backward wave layout run), a tile grid of 1 to 4 tiles per axis,
-sometimes extents that are not multiples of the tile (partial tiles: forward
-only), 1 to 3 heads with their own windows of 1 to grid + 1 tiles (wider
-than the grid is clamped), head_dim 64 or 128, bf16 or fp32 inputs and batch
-1 or 2.  Every token is compared with the oracles: the forward output to
-max 2e-2 / mean 2e-3 absolute; the row log-sum-exp to 1e-3; each gradient to
-max 2e-2 / mean 2e-3 of its rms, with the backward oracle fed the values the
-kernels consume for fp32 inputs (q, k as bf16; v, dout as fp16).
+Twelve seeded cases draw a tile shape (volumes 32 to 384, so both forward
+variants and every backward wave layout run), a tile grid of 1 to 4 tiles
+per axis, sometimes extents that are not multiples of the tile (partial
+tiles: forward only), 1 to 3 heads with their own windows of 1 to grid + 1
+tiles (wider than the grid is clamped), head_dim 64 or 128, bf16 or fp32
+inputs and batch 1 or 2; two fixed cases add 384-token tiles on a multi-tile
+grid at d64 (bf16) and d128 (fp32).  Every token is compared with the
+oracles: the forward output to max 2e-2 / mean 2e-3 absolute; the row
+log-sum-exp to 1e-3; each gradient to max 2e-2 / mean 2e-3 of its rms, with
+the backward oracle fed the values the kernels consume for fp32 inputs
+(q, k as bf16; v, dout as fp16).
 """
 
 import sys
@@ -60,7 +62,12 @@ def random_cases(n=12, seed=2024):
     return cases
 
 
-CASES = random_cases()
+CASES = random_cases() + [
+    # 384-token tiles on a multi-tile grid: d64 bf16 and d128 fp32 (the
+    # 384-query forward and the 4-wave dQ / 6-pair dK/dV kernels)
+    (Workload("fixed-384-d64", 230, (12, 16, 16), (6, 8, 8), ((1, 2, 2), (2, 1, 2)), 64, "bf16"), False),
+    (Workload("fixed-384-f32", 231, (12, 16, 16), (6, 8, 8), ((2, 2, 1), (1, 1, 1)), 128, "f32"), False),
+]
 
 
 def consumed(q, k, v, g):
