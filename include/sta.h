@@ -92,7 +92,10 @@ typedef struct {
  *   tile:   3 ints (tT, tH, tW) in tokens.
  * Errors: STA_ERR_ARG (null, non-positive sizes or windows), STA_ERR_SHAPE
  * (T, H or W not a multiple of its tile size), STA_ERR_UNSUPPORTED (head_dim
- * not 64 or 128, tile volume not a multiple of 32), STA_ERR_ALLOC.
+ * not 64 or 128; tile volume not a multiple of 32 or above 4096;
+ * batch*heads*T*H*W above INT32_MAX; more than INT32_MAX (head, query tile,
+ * key tile) pairs; a key-tile list too long for the forward kernel's LDS),
+ * STA_ERR_ALLOC.
  * On success *out owns the plan; release it with sta_plan_destroy. */
 sta_status sta_plan_create(int batch, int heads, int T, int H, int W, const int tile[3],
                            const int *window, int head_dim, sta_plan **out);

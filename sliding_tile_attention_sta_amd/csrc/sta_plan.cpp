@@ -33,7 +33,8 @@ inline int window_start(int c, int w, int n) {
 // hands blocks to free compute units in order, which is list scheduling of a
 // decreasing-cost list.  Chunks keep spatially adjacent tiles of one head on
 // the same XCD, whose L2 then serves their overlapping windows.
-std::vector<int32_t> build_schedule(const sta_plan *p, const std::vector<int32_t> &off, int subs) {
+template <typename Off>
+std::vector<int32_t> build_schedule(const sta_plan *p, const std::vector<Off> &off, int subs) {
   const int64_t n_items = (int64_t)p->batch * p->heads * p->n_tiles * subs;
   std::vector<int64_t> order(n_items);
   std::iota(order.begin(), order.end(), 0);
@@ -41,7 +42,7 @@ std::vector<int32_t> build_schedule(const sta_plan *p, const std::vector<int32_t
     int64_t rest = code / subs;
     int t = (int)(rest % p->n_tiles);
     int h = (int)((rest / p->n_tiles) % p->heads);
-    return off[h * p->n_tiles + t + 1] - off[h * p->n_tiles + t];
+    return (int64_t)off[(size_t)h * p->n_tiles + t + 1] - off[(size_t)h * p->n_tiles + t];
   };
   std::stable_sort(order.begin(), order.end(),
                    [&](int64_t a, int64_t b) { return cost(a) > cost(b); });
@@ -85,6 +86,29 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
   const int64_t N64 = (int64_t)T * H * W;
   // Element offsets are 64-bit in the kernels; token rows and table entries are int32.
   if (N64 * batch * heads > (int64_t)INT32_MAX) return STA_ERR_UNSUPPORTED;
+  // Size checks before any list is built.  Every clamped window holds the
+  // same number of key tiles for each query tile of its head.  The lists of
+  // all heads sit in one table indexed by int32 offsets (as do their
+  // inverses, which hold as many entries), and the longest list must fit the
+  // forward kernel's LDS beside its K/V stages.
+  {
+    int64_t grid[3], pairs = 0, longest = 0;
+    bool partial = false;
+    for (int d = 0; d < 3; ++d) {
+      grid[d] = (ext[d] + tile[d] - 1) / tile[d];
+      partial |= ext[d] % tile[d] != 0;
+    }
+    const int64_t n_tiles = grid[0] * grid[1] * grid[2];
+    for (int h = 0; h < heads && pairs <= (int64_t)INT32_MAX; ++h) {
+      int64_t vol = 1;
+      for (int d = 0; d < 3; ++d) vol *= std::min<int64_t>(window[h * 3 + d], grid[d]);
+      longest = std::max(longest, vol);
+      pairs += n_tiles * vol;
+    }
+    if (pairs > (int64_t)INT32_MAX) return STA_ERR_UNSUPPORTED;
+    if (fwd_lds_bytes(head_dim, V64, longest) + (partial ? 4LL * longest * (V64 / kKeyBlock) : 0) > kMaxLds)
+      return STA_ERR_UNSUPPORTED;
+  }
 
   sta_plan *p = new (std::nothrow) sta_plan();
   if (!p) return STA_ERR_ALLOC;
@@ -262,7 +286,7 @@ sta_status build_swa_plan(int batch, int heads, int T, int H, int W, const int t
     // Work per (head, query tile): rows (t, y) of the union of the tile's
     // query windows times the 32-key runs covering its z range.
     auto start = [](int x, int w, int e) { return std::min(std::max(x - (w - 1) / 2, 0), e - w); };
-    std::vector<int32_t> cost_off((size_t)heads * p->n_tiles + 1, 0);
+    std::vector<int64_t> cost_off((size_t)heads * p->n_tiles + 1, 0);
     const int nH = p->grid[1], nW = p->grid[2];
     for (int h = 0; h < heads; ++h)
       for (int qt = 0; qt < p->n_tiles; ++qt) {
@@ -275,7 +299,7 @@ sta_status build_swa_plan(int batch, int heads, int T, int H, int W, const int t
           span[d] = hi - lo;
         }
         const int64_t steps = span[0] * span[1] * ((span[2] + kKeyBlock - 1) / kKeyBlock);
-        cost_off[(size_t)h * p->n_tiles + qt + 1] = cost_off[(size_t)h * p->n_tiles + qt] + (int32_t)steps;
+        cost_off[(size_t)h * p->n_tiles + qt + 1] = cost_off[(size_t)h * p->n_tiles + qt] + steps;
       }
     p->kv_off.assign((size_t)heads * p->n_tiles + 1, 0);
     p->q_off.assign((size_t)heads * p->n_tiles + 1, 0);

@@ -143,6 +143,14 @@ def test_plan_create_errors():
     assert _create(1, 1, 6, 16, 16, t, None, 64) == L.STA_ERR_ARG
     assert _create(1, 1, 6, 16, 16, _ints([2, 0, 4]), w1, 64) == L.STA_ERR_ARG
     assert L.lib().sta_plan_create(1, 1, 6, 16, 16, t, w1, 64, None) == L.STA_ERR_ARG
+    # size limits, all rejected before any list is built (each call returns at once)
+    t32 = _ints([1, 1, 32])
+    assert _create(1, 1, 4, 32, 64, _ints([4, 32, 64]), w1, 64) == L.STA_ERR_UNSUPPORTED  # 8192 tokens/tile
+    assert _create(2, 1, 1, 2048, 1 << 20, t32, w1, 64) == L.STA_ERR_UNSUPPORTED  # 2^32 rows
+    # 2^21 tiles x 33 x 33 key tiles each: more (query, key) tile pairs than int32 offsets reach
+    assert _create(1, 1, 1, 2048, 32768, t32, _ints([1, 33, 33]), 64) == L.STA_ERR_UNSUPPORTED
+    # 40,000 key tiles per list (1.6e9 pairs): the list outgrows the forward kernel's LDS
+    assert _create(1, 1, 1, 200, 6400, t32, _ints([1, 200, 200]), 64) == L.STA_ERR_UNSUPPORTED
     assert L.lib().sta_plan_destroy(None) == L.STA_OK
 
 
