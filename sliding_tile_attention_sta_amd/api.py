@@ -56,6 +56,20 @@ def _on(stream):
     return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
+@contextlib.contextmanager
+def _scope(tensors, stream):
+    """Every tensor of a call (and its stream, if given) must be on one
+    device; the call allocates and launches with that device current."""
+    dev = tensors[0].device
+    for x in tensors[1:]:
+        if x is not None and x.device != dev:
+            raise ValueError(f"all tensors must be on {dev} (found {x.device})")
+    if stream is not None and stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {dev}")
+    with torch.cuda.device(dev), _on(stream):
+        yield
+
+
 class Plan:
     """Owned sta_plan handle (host tables; device tables are uploaded lazily)."""
 
@@ -156,14 +170,14 @@ def _check_tensor(x: torch.Tensor, plan: Plan, name: str):
 
 def _reorder(fn, plan: Plan, x: torch.Tensor, out, stream):
     _check_tensor(x, plan, "x")
-    if out is None:
-        with _on(stream):
+    with _scope([x, out], stream):
+        if out is None:
             out = torch.empty_like(x)
-    _check_tensor(out, plan, "out")
-    if out.dtype != x.dtype:
-        raise ValueError("out must have the input's dtype")
-    L.check(fn(plan.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
-               _DTYPES[x.dtype], _stream(stream)), fn.__name__)
+        _check_tensor(out, plan, "out")
+        if out.dtype != x.dtype:
+            raise ValueError("out must have the input's dtype")
+        L.check(fn(plan.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                   _DTYPES[x.dtype], _stream(stream)), fn.__name__)
     return out
 
 
@@ -198,23 +212,22 @@ def sta_forward_plan(plan: Plan, q, k, v, out=None, scale: float | None = None,
         _check_tensor(x, plan, name)
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
-    if out is None:
-        with _on(stream):
-            out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    _check_tensor(out, plan, "out")
     if scale is None:
         scale = 1.0 / math.sqrt(plan.info.head_dim)
-    args = (plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out))
-    tail = (float(scale), _DTYPES[q.dtype], _DTYPES[out.dtype], _LAYOUTS[layout], _stream(stream))
-    if lse is None or lse is False:
-        L.check(L.lib().sta_forward_plan(*args, *tail), "sta_forward_plan")
-        return out
-    if lse is True:
-        i = plan.info
-        with _on(stream):
+    with _scope([q, k, v, out, lse if isinstance(lse, torch.Tensor) else None], stream):
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        _check_tensor(out, plan, "out")
+        args = (plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out))
+        tail = (float(scale), _DTYPES[q.dtype], _DTYPES[out.dtype], _LAYOUTS[layout], _stream(stream))
+        if lse is None or lse is False:
+            L.check(L.lib().sta_forward_plan(*args, *tail), "sta_forward_plan")
+            return out
+        if lse is True:
+            i = plan.info
             lse = torch.empty((i.batch, i.heads, i.tokens), dtype=torch.float32, device=q.device)
-    _check_rows(lse, plan, "lse")
-    L.check(L.lib().sta_forward_plan_lse(*args, _ptr(lse), *tail), "sta_forward_plan_lse")
+        _check_rows(lse, plan, "lse")
+        L.check(L.lib().sta_forward_plan_lse(*args, _ptr(lse), *tail), "sta_forward_plan_lse")
     return out, lse
 
 
@@ -229,26 +242,25 @@ def sta_backward_plan(plan: Plan, q, k, v, out, dout, lse, scale: float | None =
         raise ValueError("q, k, v, dout must share a dtype")
     _check_rows(lse, plan, "lse")
     i = plan.info
-    if delta is None:
-        with _on(stream):
-            delta = torch.empty((i.batch, i.heads, i.tokens), dtype=torch.float32, device=q.device)
-    _check_rows(delta, plan, "delta")
-    grads = []
-    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
-        if g is None:
-            with _on(stream):
-                g = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
-        _check_tensor(g, plan, name)
-        grads.append(g)
-    if not (grads[0].dtype == grads[1].dtype == grads[2].dtype):
-        raise ValueError("dq, dk, dv must share a dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(i.head_dim)
-    st = L.lib().sta_backward_plan(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
-                                   _ptr(lse), _ptr(delta), *(_ptr(g) for g in grads), float(scale),
-                                   _DTYPES[q.dtype], _DTYPES[out.dtype], _DTYPES[grads[0].dtype],
-                                   _LAYOUTS[layout], _stream(stream))
-    L.check(st, "sta_backward_plan")
+    with _scope([q, k, v, out, dout, lse, delta, dq, dk, dv], stream):
+        if delta is None:
+            delta = torch.empty((i.batch, i.heads, i.tokens), dtype=torch.float32, device=q.device)
+        _check_rows(delta, plan, "delta")
+        grads = []
+        for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+            if g is None:
+                g = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+            _check_tensor(g, plan, name)
+            grads.append(g)
+        if not (grads[0].dtype == grads[1].dtype == grads[2].dtype):
+            raise ValueError("dq, dk, dv must share a dtype")
+        st = L.lib().sta_backward_plan(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                       _ptr(lse), _ptr(delta), *(_ptr(g) for g in grads), float(scale),
+                                       _DTYPES[q.dtype], _DTYPES[out.dtype], _DTYPES[grads[0].dtype],
+                                       _LAYOUTS[layout], _stream(stream))
+        L.check(st, "sta_backward_plan")
     return tuple(grads)
 
 
@@ -278,6 +290,27 @@ def sta_attention(q, k, v, plan: Plan, scale: float | None = None, layout: str =
     return _StaAttention.apply(q, k, v, plan, float(scale), layout)
 
 
+def _video_inputs(q, k, v, video):
+    """(B, heads, T, H, W, D) of natural-order q, k, v given as
+    [B, heads, T, H, W, D], or as [B, heads, N, D] with video=(T, H, W)."""
+    if not isinstance(q, torch.Tensor) or q.dim() not in (4, 6):
+        raise ValueError("q must be a [B, heads, T, H, W, D] or [B, heads, N, D] tensor")
+    if q.dim() == 6:
+        B, heads, T, H, W, D = q.shape
+    else:
+        if video is None:
+            raise ValueError("video=(T, H, W) is required for 4-D inputs")
+        B, heads, N, D = q.shape
+        T, H, W = (int(x) for x in video)
+        if N != T * H * W:
+            raise ValueError(f"q has {N} tokens, video {T}x{H}x{W} has {T * H * W}")
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(x, torch.Tensor) or not x.is_cuda or not x.is_contiguous() \
+                or x.dtype not in _DTYPES or x.shape != q.shape or x.dtype != q.dtype:
+            raise ValueError(f"{name}: contiguous CUDA bf16/fp32 tensor shaped like q (and of its dtype) required")
+    return B, heads, T, H, W, D
+
+
 def sta_forward(q, k, v, tile, windows, scale: float | None = None, out=None,
                 out_dtype=torch.float32, layout: str = "natural", video=None, stream=None):
     """STA forward through the library's plan cache.
@@ -285,27 +318,20 @@ def sta_forward(q, k, v, tile, windows, scale: float | None = None, out=None,
     q, k, v: [B, heads, T, H, W, D] (natural layout), or [B, heads, N, D]
     with ``video=(T, H, W)``.  windows: one (wT, wH, wW) per head (or one for
     all heads), in tiles."""
-    if q.dim() == 6:
-        B, heads, T, H, W, D = q.shape
-    else:
-        if video is None:
-            raise ValueError("video=(T, H, W) is required for 4-D inputs")
-        B, heads, _, D = q.shape
-        T, H, W = video
-    for name, x in (("q", q), ("k", k), ("v", v)):
-        if not x.is_cuda or not x.is_contiguous() or x.dtype not in _DTYPES or x.shape != q.shape:
-            raise ValueError(f"{name}: contiguous CUDA bf16/fp32 tensor shaped like q required")
-    if out is None:
-        with _on(stream):
-            out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    B, heads, T, H, W, D = _video_inputs(q, k, v, video)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    st = L.lib().sta_forward(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
-                             ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
-                             int(B), int(heads), int(T), int(H), int(W), _ints(tile),
-                             _ints(_flat_windows(windows, heads)), int(D), float(scale),
-                             _DTYPES[q.dtype], _DTYPES[out.dtype], _LAYOUTS[layout], _stream(stream))
-    L.check(st, "sta_forward")
+    with _scope([q, k, v, out], stream):
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        if not out.is_cuda or not out.is_contiguous() or out.dtype not in _DTYPES or out.numel() != q.numel():
+            raise ValueError("out: contiguous CUDA bf16/fp32 tensor with q's element count required")
+        st = L.lib().sta_forward(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                 ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                 int(B), int(heads), int(T), int(H), int(W), _ints(tile),
+                                 _ints(_flat_windows(windows, heads)), int(D), float(scale),
+                                 _DTYPES[q.dtype], _DTYPES[out.dtype], _LAYOUTS[layout], _stream(stream))
+        L.check(st, "sta_forward")
     return out
 
 
@@ -325,26 +351,19 @@ def window_errors(q, k, v, tile, candidates, scale: float | None = None, layout:
     each candidate window, on one calibration input (natural
     [B, heads, T, H, W, D], or [B, heads, N, D] with video=(T, H, W))."""
     import numpy as np
-    if q.dim() == 6:
-        B, heads, T, H, W, D = q.shape
-    else:
-        if video is None:
-            raise ValueError("video=(T, H, W) is required for 4-D inputs")
-        B, heads, _, D = q.shape
-        T, H, W = video
-    for name, x in (("q", q), ("k", k), ("v", v)):
-        if not x.is_cuda or not x.is_contiguous() or x.dtype not in _DTYPES or x.shape != q.shape \
-                or x.dtype != q.dtype:
-            raise ValueError(f"{name}: contiguous CUDA bf16/fp32 tensor shaped like q required")
-    cands = [int(x) for w in candidates for x in w]
-    n = len(cands) // 3
+    B, heads, T, H, W, D = _video_inputs(q, k, v, video)
+    cands = [tuple(int(x) for x in w) for w in candidates]
+    if not cands or any(len(w) != 3 for w in cands):
+        raise ValueError("candidates: one or more (wT, wH, wW) windows")
+    n = len(cands)
     err = (ctypes.c_double * (heads * n))()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    st = L.lib().sta_window_errors(_ptr(q), _ptr(k), _ptr(v), int(B), int(heads), int(T), int(H), int(W),
-                                   _ints(tile), int(D), float(scale), _DTYPES[q.dtype], _LAYOUTS[layout],
-                                   _ints(cands), n, err, _stream(stream))
-    L.check(st, "sta_window_errors")
+    with _scope([q, k, v], stream):
+        st = L.lib().sta_window_errors(_ptr(q), _ptr(k), _ptr(v), int(B), int(heads), int(T), int(H), int(W),
+                                       _ints(tile), int(D), float(scale), _DTYPES[q.dtype], _LAYOUTS[layout],
+                                       _ints([x for w in cands for x in w]), n, err, _stream(stream))
+        L.check(st, "sta_window_errors")
     return np.array(err[:], dtype=np.float64).reshape(heads, n)
 
 
@@ -372,6 +391,8 @@ def window_search(samples, tile, threshold: float, candidates=None, scale: float
     errors, candidates)."""
     errs, video = [], None
     for q, k, v in samples:
+        if video is not None and tuple(q.shape[2:5]) != video:
+            raise ValueError("calibration samples must share one video shape")
         video = tuple(q.shape[2:5])
         grid = tuple(e // t for e, t in zip(video, tile))
         cands = candidates if candidates is not None else window_candidates(grid)
