@@ -32,8 +32,9 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed calls (default 50; 3 for the window search, whose sweep takes seconds)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed calls first (default 10; 1 for search)")
     ap.add_argument("--workload", default="720p")
     ap.add_argument("--pass", dest="which", choices=["forward", "backward", "search", "swa"],
                     default="forward",
@@ -48,7 +49,13 @@ def parse():
                          "used to calibrate HBM traffic counters")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                            "profiles", "traffic.json"))
-    return ap.parse_args()
+    args = ap.parse_args()
+    search = args.which == "search"
+    if args.steps is None:
+        args.steps = 3 if search else 50
+    if args.warmup is None:
+        args.warmup = 1 if search else 10
+    return args
 
 
 def timed(fn, steps, warmup, stream):
