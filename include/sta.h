@@ -129,8 +129,11 @@ sta_status sta_plan_create_ex(int batch, int heads, int T, int H, int W, const i
 sta_status sta_swa_plan_create(int batch, int heads, int T, int H, int W, const int tile[3],
                                const int *window_tokens, int head_dim, sta_plan **out);
 
-/* Release a plan and its device tables (NULL is a no-op).  The caller must
- * make sure no launched work still uses the plan. */
+/* Release a plan and its device tables (NULL is a no-op).  Before freeing
+ * the tables on a device it waits for all work queued on that device
+ * (hipDeviceSynchronize), so a plan may be released right after launching
+ * work with it; it must not be released while another host thread is still
+ * launching with it. */
 sta_status sta_plan_destroy(sta_plan *plan);
 
 /* Copy the plan description into *info (host). */

@@ -113,8 +113,12 @@ void release_device_tables(sta_plan *p) {
   if (p->dev.empty()) return;
   int cur = -1;
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  // Work launched with the plan may still read its tables: each device
+  // finishes its queued work before its copy is freed.
   for (auto &kv : p->dev) {
-    if (hipSetDevice(kv.first) == hipSuccess) (void)hipFree(kv.second.block);
+    if (hipSetDevice(kv.first) != hipSuccess) continue;
+    (void)hipDeviceSynchronize();
+    (void)hipFree(kv.second.block);
   }
   if (have_cur) (void)hipSetDevice(cur);
   p->dev.clear();

@@ -2,7 +2,9 @@
 is given.  The inputs are copied on a side stream behind a bounded spin
 kernel, and the calls are made with that stream while the current stream is
 the default one: a launch on any other stream would read inputs that are
-not written yet, so the outputs are compared bit for bit with a plain run."""
+not written yet, so the outputs are compared bit for bit with a plain run.
+A plan released right after a launch (its forward still queued behind a
+spin) gives the same bits as one that stays alive."""
 
 import sys
 
@@ -39,3 +41,18 @@ def test_entry_points_run_on_the_given_stream():
     for a, b in ((dq2, dq), (dk2, dk), (dv2, dv)):
         assert torch.equal(a, b)
     assert torch.equal(tm2, tm)
+
+
+def test_plan_released_right_after_launch():
+    print("case small workload: plan released while its forward is queued", file=sys.stderr, flush=True)
+    w = WORKLOADS["small"]
+    keep = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    q, k, v = (x.cuda() for x in make_qkv(w))
+    ref = api.sta_forward_plan(keep, q, k, v, scale=w.scale)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)   # the forward below queues behind this bounded spin
+    tmp = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    out = api.sta_forward_plan(tmp, q, k, v, scale=w.scale)
+    del tmp                         # sta_plan_destroy waits for the queued work first
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
