@@ -250,9 +250,18 @@ def _cpu_model():
     return "unknown"
 
 
+def _build_flags(source):
+    """The compiler flags of one HIP source (include paths left out: they
+    name the checkout's location)."""
+    from sliding_tile_attention_sta_amd import build as B
+    flags = [f for i, f in enumerate(B.HIP_FLAGS) if f != "-I" and (i == 0 or B.HIP_FLAGS[i - 1] != "-I")]
+    return flags + list(B.HIP_EXTRA.get(source, []))
+
+
 def _measured_traffic(path, source, workload, key):
     """HBM bytes from a committed rocprofv3 counter summary, used only while
-    the kernel source hashes to the one measured (else None)."""
+    the kernel source hashes to the one measured and is built with the same
+    flags (else None)."""
     try:
         with open(path) as f:
             t = json.load(f)
@@ -261,7 +270,8 @@ def _measured_traffic(path, source, workload, key):
             digest = hashlib.sha256(f.read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if t.get("workload") == workload and t.get("kernel_source_sha256") == digest:
+    if t.get("workload") == workload and t.get("kernel_source_sha256") == digest \
+            and t.get("kernel_build_flags") == _build_flags(source):
         return t.get(key)
     return None
 
