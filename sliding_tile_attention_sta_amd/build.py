@@ -28,10 +28,13 @@ HIP_SOURCES = ["sta_api.hip", "sta_forward.hip", "sta_backward.hip", "sta_reorde
 # Per-file extra flags.  The forward kernel needs no IEEE signalling-NaN
 # quieting, which lets v_max_f32 read MFMA results without canonicalising them.
 # Its instructions are scheduled with the AMDGPU-specific register-pressure
-# trackers (measured 0.3-0.5 % faster on the 720p forward, same 236 VGPRs;
-# the backward kernels ran 0.6 % slower with them and keep the default).
+# trackers and without the scheduler's clustered low-occupancy rescheduling
+# stage (measured 0.3-0.5 % and a further 0.5-1 % faster on the 720p
+# forward, same 236 VGPRs; the backward kernels ran 0.6 % slower with the
+# trackers and keep the default).
 HIP_EXTRA = {"sta_forward.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
-                                 "-mllvm", "-amdgpu-use-amdgpu-trackers"]}
+                                 "-mllvm", "-amdgpu-use-amdgpu-trackers",
+                                 "-mllvm", "-amdgpu-disable-clustered-low-occupancy-reschedule"]}
 CXX_SOURCES = ["sta_plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")
