@@ -380,3 +380,35 @@ def test_swa_plan_info_and_unsupported_paths():
                                    ctypes.byref(h)) == L.STA_ERR_SHAPE
     assert lib.sta_swa_plan_create(1, 1, 30, 48, 80, _ints([6, 8, 8]), _ints([3, 0, 3]), 128,
                                    ctypes.byref(h)) == L.STA_ERR_ARG
+
+
+def test_swa_schedule_with_cost_sums_beyond_int32():
+    # 24 heads x 4096 query tiles x ~32k key steps: the per-item cost prefix
+    # sums pass 2^31; every XCD queue must still run in decreasing cost.
+    import numpy as np
+    video, tile, win, heads = (64, 128, 128), (4, 8, 8), (63, 127, 127), 24
+    p = api.Plan(1, heads, video, tile, [win], 128, token_windows=True)
+    info = p.info
+    grid = [e // t for e, t in zip(video, tile)]
+
+    def start(x, w, e):
+        return np.minimum(np.maximum(x - (w - 1) // 2, 0), e - w)
+
+    c = np.stack(np.meshgrid(*(np.arange(g) for g in grid), indexing="ij"), -1).reshape(-1, 3)
+    span = [start(c[:, d] * tile[d] + tile[d] - 1, win[d], video[d]) + win[d] - start(c[:, d] * tile[d], win[d], video[d])
+            for d in range(3)]
+    cost_tile = span[0] * span[1] * ((span[2] + 31) // 32)
+    assert int(cost_tile.sum()) * heads > 2 ** 31
+    s = p.schedule().numpy()
+    codes = s[s >= 0]
+    n_items = codes.size
+    assert np.array_equal(np.sort(codes), np.arange(n_items))
+    subs = n_items // (heads * info.n_tiles)
+    assert subs * heads * info.n_tiles == n_items
+    cost = cost_tile[(codes // subs) % info.n_tiles]
+    full = np.full(s.shape, -1, dtype=np.int64)
+    full[s >= 0] = cost
+    for x in range(8):
+        q = full[x::8]
+        q = q[q >= 0]
+        assert np.all(np.diff(q) <= 0)
