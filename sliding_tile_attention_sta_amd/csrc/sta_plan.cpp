@@ -203,21 +203,24 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
     // tiles visit them at the same step.
     p->q_off.assign((size_t)heads * p->n_tiles + 1, 0);
     {
+      // Query tiles are visited in (residue, raster) order and appended to
+      // the lists of their key tiles, so every list comes out in that order.
       std::vector<std::vector<int32_t>> inv(p->n_tiles);
+      std::vector<int32_t> res(p->n_tiles), by_res(p->n_tiles);
       for (int h = 0; h < heads; ++h) {
         for (auto &v : inv) v.clear();
-        for (int qt = 0; qt < p->n_tiles; ++qt) {
+        const int *w = &p->win[h * 3];
+        for (int t = 0; t < p->n_tiles; ++t) {
+          const int ct = t / (nH * nW), cy = (t / nW) % nH, cz = t % nW;
+          res[t] = ((ct % w[0]) * w[1] + cy % w[1]) * w[2] + cz % w[2];
+        }
+        std::iota(by_res.begin(), by_res.end(), 0);
+        std::stable_sort(by_res.begin(), by_res.end(), [&](int32_t x, int32_t y) { return res[x] < res[y]; });
+        for (const int32_t qt : by_res) {
           const size_t i = (size_t)h * p->n_tiles + qt;
           for (int32_t e = p->kv_off[i]; e < p->kv_off[i + 1]; ++e) inv[p->kv_idx[e]].push_back(qt);
         }
-        const int *w = &p->win[h * 3];
-        auto residue = [&](int32_t t) {
-          const int ct = t / (nH * nW), cy = (t / nW) % nH, cz = t % nW;
-          return ((ct % w[0]) * w[1] + cy % w[1]) * w[2] + cz % w[2];
-        };
         for (int kt = 0; kt < p->n_tiles; ++kt) {
-          std::stable_sort(inv[kt].begin(), inv[kt].end(),
-                           [&](int32_t x, int32_t y) { return residue(x) < residue(y); });
           p->q_idx.insert(p->q_idx.end(), inv[kt].begin(), inv[kt].end());
           p->q_off[(size_t)h * p->n_tiles + kt + 1] = (int32_t)p->q_idx.size();
           p->max_nq = std::max(p->max_nq, (int32_t)inv[kt].size());
