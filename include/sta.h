@@ -82,6 +82,10 @@ typedef struct {
   int64_t bwd_items_dkdv;   /* launched dK/dV work items (including idle padding) */
   int32_t partial_tiles;    /* 1 if some extent is not a multiple of its tile size */
   int32_t swa;              /* 1 for a token-wise sliding-window plan (sta_swa_plan_create) */
+  int32_t split_items;      /* forward work items split by key range (0 = none) */
+  int32_t pieces;           /* launched pieces of those items */
+  int64_t scratch_bytes;    /* device scratch a forward launch of this plan uses (0 = none) */
+  int64_t launch_blocks;    /* work groups of one forward launch */
 } sta_plan_info;
 
 /* Build the host plan: tile grid, clamped per-head windows, per-(head, query
@@ -155,11 +159,31 @@ sta_status sta_plan_kv_tiles(const sta_plan *plan, int head, int q_tile, int32_t
 sta_status sta_plan_q_tiles(const sta_plan *plan, int head, int kv_tile, int32_t *out, int cap,
                             int *count);
 
-/* The launch schedule: item codes in launch order, -1 for idle padding items.
- * A code encodes ((b * heads + h) * n_tiles + q_tile) * subs + sub, where
- * subs = tile_tokens / queries_per_item.  out: host buffer of cap int32;
- * *count receives the item count (STA_ERR_ARG if it exceeds cap). */
+/* The forward's work queues, one per XCD (accelerator complex die) of the
+ * chip, interleaved: entry s * 8 + x is the s-th entry of XCD x's queue,
+ * -1 where that queue is shorter than the longest.  Other entries are item
+ * codes, or -2 - p for piece p of a split item (see sta_plan_pieces).  A
+ * code >= 0 encodes ((b * heads + h) * n_tiles + q_tile) * subs + sub,
+ * where subs = tile_tokens / queries_per_item.  With the 384-query kernel
+ * (info.kernel_variant 1) the queues are consumed dynamically: each work
+ * group takes the next entry of its own XCD's queue, or, once that queue
+ * is empty, of another's, so a faster XCD takes more of the work; otherwise
+ * work group b runs entry b.  out: host buffer of cap int32; *count
+ * receives the entry count (STA_ERR_ARG if it exceeds cap). */
 sta_status sta_plan_schedule(const sta_plan *plan, int32_t *out, int64_t cap, int64_t *count);
+
+/* The pieces of split work items (info.pieces of them).  A work item of the
+ * forward walks its key tiles' 32-key blocks in order, steps
+ * 0 .. key_tiles * tile_tokens / 32 - 1; when equal-cost items would leave
+ * the last round of a launch to a few compute units, the plan cuts those
+ * items into pieces of consecutive steps that run side by side, and the
+ * last piece of an item to finish combines the pieces' partial softmax
+ * results (exact up to fp32 rounding: each piece's unnormalised output and
+ * row sums are rescaled to the largest of their reference maxima).
+ * out: host buffer of cap * 5 int32, per piece (item code, first step, end
+ * step, item index among the split items, pieces of that item); *count
+ * receives the piece count (STA_ERR_ARG if it exceeds cap). */
+sta_status sta_plan_pieces(const sta_plan *plan, int32_t *out, int64_t cap, int64_t *count);
 
 /* The backward schedules, same conventions: which = 0 for the dQ kernel
  * (code ((b * heads + h) * n_tiles + q_tile) * subs + sub, subs =

@@ -29,7 +29,8 @@ class PlanInfo(ctypes.Structure):
         ("bwd_queries_per_item", ctypes.c_int32), ("bwd_keys_per_item", ctypes.c_int32),
         ("bwd_items_dq", ctypes.c_int64),
         ("bwd_items_dkdv", ctypes.c_int64), ("partial_tiles", ctypes.c_int32),
-        ("swa", ctypes.c_int32),
+        ("swa", ctypes.c_int32), ("split_items", ctypes.c_int32), ("pieces", ctypes.c_int32),
+        ("scratch_bytes", ctypes.c_int64), ("launch_blocks", ctypes.c_int64),
     ]
 
 
@@ -49,6 +50,7 @@ SIGNATURES = {
     "sta_plan_perm": (_I, [_P, _I32P, _I64]),
     "sta_plan_kv_tiles": (_I, [_P, _I, _I, _I32P, _I, _IP]),
     "sta_plan_schedule": (_I, [_P, _I32P, _I64, ctypes.POINTER(_I64)]),
+    "sta_plan_pieces": (_I, [_P, _I32P, _I64, ctypes.POINTER(_I64)]),
     "sta_plan_q_tiles": (_I, [_P, _I, _I, _I32P, _I, _IP]),
     "sta_plan_schedule_bwd": (_I, [_P, _I, _I32P, _I64, ctypes.POINTER(_I64)]),
     "sta_tile_reorder": (_I, [_P, _P, _P, _I, _P]),

@@ -151,6 +151,16 @@ class Plan:
                                           ctypes.byref(n)), "sta_plan_schedule")
         return out
 
+    def pieces(self) -> torch.Tensor:
+        """[pieces, 5] int32: (item code, first step, end step, split item,
+        pieces of that item) of every piece of a split work item."""
+        n = ctypes.c_int64()
+        L.lib().sta_plan_pieces(self._h, None, 0, ctypes.byref(n))
+        out = torch.empty((max(1, n.value), 5), dtype=torch.int32)
+        L.check(L.lib().sta_plan_pieces(self._h, ctypes.cast(out.data_ptr(), L._I32P), n.value,
+                                        ctypes.byref(n)), "sta_plan_pieces")
+        return out[:n.value]
+
 
 def sta_plan_create(batch, heads, video, tile, windows, head_dim) -> Plan:
     return Plan(batch, heads, video, tile, windows, head_dim)

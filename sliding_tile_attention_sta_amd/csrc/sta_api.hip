@@ -36,7 +36,7 @@ sta_status device_tables(const sta_plan *p, DeviceTables *out) {
   const std::vector<int32_t> *parts[] = {&p->kv_off, &p->kv_idx,   &p->sched,    &p->base_nat,
                                          &p->off_nat, &base_tm,     &off_tm,      &p->q_off,
                                          &p->q_idx,   &p->sched_dq, &p->sched_dkdv, &p->kmask,
-                                         &p->swin};
+                                         &p->swin,    &p->ptab,     &p->gtab,     &p->queue};
   constexpr int kParts = sizeof(parts) / sizeof(parts[0]);
   size_t offs[kParts], total = 0;
   for (int i = 0; i < kParts; ++i) {
@@ -68,9 +68,45 @@ sta_status device_tables(const sta_plan *p, DeviceTables *out) {
   t.sched_dkdv = reinterpret_cast<int32_t *>(b + offs[10]);
   t.kmask = p->kmask.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[11]);
   t.swin = p->swin.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[12]);
+  t.ptab = p->ptab.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[13]);
+  t.gtab = p->gtab.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[14]);
+  t.queue = p->queue.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[15]);
   t.block = block;
   p->dev[dev] = t;
   *out = t;
+  return STA_OK;
+}
+
+// The forward scratch of a plan with dynamic queues on the current device,
+// for launches on `stream` (allocated on first use; its counters are
+// cleared once, in stream order, and every launch leaves them zero).
+sta_status forward_scratch(const sta_plan *p, void *stream, void **out) {
+  *out = nullptr;
+  if (p->dyn_blocks == 0) return STA_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return STA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(p->mu);
+  const auto key = std::make_pair(dev, stream);
+  auto it = p->scratch.find(key);
+  if (it != p->scratch.end()) {
+    *out = it->second;
+    return STA_OK;
+  }
+  void *buf = nullptr;
+  if (hipMalloc(&buf, (size_t)fwd_scratch_bytes(p->D, p->n_groups, p->n_pieces)) != hipSuccess)
+    return STA_ERR_ALLOC;
+  if (launch_zero(static_cast<int32_t *>(buf), kQueueWords + p->n_groups, static_cast<hipStream_t>(stream)) !=
+      hipSuccess) {
+    (void)hipFree(buf);
+    return STA_ERR_HIP;
+  }
+  try {
+    p->scratch[key] = buf;
+  } catch (...) {
+    (void)hipFree(buf);
+    return STA_ERR_ALLOC;
+  }
+  *out = buf;
   return STA_OK;
 }
 
@@ -110,18 +146,25 @@ std::map<CacheKey, sta_plan *> g_cache;
 
 void release_device_tables(sta_plan *p) {
   std::lock_guard<std::mutex> lock(p->mu);
-  if (p->dev.empty()) return;
+  if (p->dev.empty() && p->scratch.empty()) return;
   int cur = -1;
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
-  // Work launched with the plan may still read its tables: each device
-  // finishes its queued work before its copy is freed.
-  for (auto &kv : p->dev) {
-    if (hipSetDevice(kv.first) != hipSuccess) continue;
+  // Work launched with the plan may still read its tables and scratch: each
+  // device finishes its queued work before its buffers are freed.
+  std::map<int, bool> synced;
+  auto sync = [&](int dev) {
+    if (synced[dev]) return true;
+    if (hipSetDevice(dev) != hipSuccess) return false;
     (void)hipDeviceSynchronize();
-    (void)hipFree(kv.second.block);
-  }
+    return synced[dev] = true;
+  };
+  for (auto &kv : p->dev)
+    if (sync(kv.first)) (void)hipFree(kv.second.block);
+  for (auto &kv : p->scratch)
+    if (sync(kv.first.first)) (void)hipFree(kv.second);
   if (have_cur) (void)hipSetDevice(cur);
   p->dev.clear();
+  p->scratch.clear();
 }
 
 }  // namespace sta
@@ -163,6 +206,9 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   sta::DeviceTables t;
   sta_status st = sta::device_tables(p, &t);
   if (st != STA_OK) return st;
+  void *scratch = nullptr;
+  st = forward_scratch(p, stream, &scratch);
+  if (st != STA_OK) return st;
   sta::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = out;
   a.sched = t.sched;
@@ -184,6 +230,16 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   a.T = p->T; a.H = p->H; a.W = p->W;
   a.tT = p->tile[0]; a.tH = p->tile[1]; a.tW = p->tile[2];
   a.gH = p->grid[1]; a.gW = p->grid[2];
+  a.queue = t.queue;
+  for (int x = 0; x < 10; ++x) a.qoff[x] = p->qoff[x];
+  a.qcount = static_cast<int32_t *>(scratch);
+  if (p->dyn_blocks) a.n_blocks = p->dyn_blocks;
+  a.ptab = t.ptab;
+  a.gtab = t.gtab;
+  a.pcount = scratch ? a.qcount + kQueueWords : nullptr;
+  a.pslot = scratch && p->n_pieces
+                ? reinterpret_cast<float *>(static_cast<char *>(scratch) + fwd_counter_bytes(p->n_groups))
+                : nullptr;
   hipError_t e = sta::launch_forward(a, p->variant, p->D, in_dtype == STA_F32, out_dtype == STA_F32,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? STA_OK : STA_ERR_HIP;

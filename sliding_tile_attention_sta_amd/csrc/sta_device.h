@@ -12,18 +12,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) char lds_char;
-
-// Lazy rescaling of the online softmax: the running reference max only moves
-// when a block's max exceeds it by more than 2^kTau in exp2 units, so
-// probabilities stay <= 2^kTau (comfortably inside fp16) and O is rarely
-// rescaled.
-constexpr float kTau = 8.f;
 
 // Raw global data of one 8-element chunk (converted when written to LDS, so
 // that the global loads of the next step stay in flight during the math).

@@ -112,21 +112,67 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   int *off_l = reinterpret_cast<int *>(smem + 2 * KST_BYTES + 2 * VST_BYTES);
   int *kvb_l = off_l + a.V;
 
-  // The work item is uniform: readfirstlane keeps it and everything derived
-  // from it in SGPRs.
-  const int item = __builtin_amdgcn_readfirstlane(a.sched[blockIdx.x]);
-  if (item < 0) return;
-  const int sub = item % a.subs;
-  const int rest = item / a.subs;
-  const int qt = rest % a.n_tiles;
-  const int bh = rest / a.n_tiles;
-  const int h = bh % a.heads;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int g = lane >> 4;
+
+  // The work item.  Dynamic queues: thread 0 takes the next entry of its
+  // XCD's queue (hardware register XCC_ID), or of the next XCD queue that
+  // is not empty, or else of the piece queue, and shares it through LDS; a
+  // work group that finds every queue empty exits (and sets a flag that
+  // lets later ones exit at once).  Every work group counts itself out at
+  // its end, and the last one zeroes the queue words for the next launch.
+  // The item is uniform: readfirstlane keeps it and everything derived from
+  // it in SGPRs.  A piece of a split item walks steps [s_first, s_end) of
+  // the item's key blocks.
+  int item;
+  if (a.queue != nullptr) {
+    __shared__ int taken;
+    if (tid == 0) {
+      int code = -1;
+      const int x = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);   // HW_REG_XCC_ID[3:0]
+      for (int t = 0; t < 9; ++t) {
+        const int y = t == 8 ? 8 : (x + t) & 7;
+        const int n = a.qoff[y + 1] - a.qoff[y];
+        if (n == 0) continue;
+        if (t == 1 && __hip_atomic_load(a.qcount + 10, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+        const int i = atomicAdd(a.qcount + y, 1);
+        if (i < n) {
+          code = a.queue[a.qoff[y] + i];
+          break;
+        }
+      }
+      if (code == -1) __hip_atomic_store(a.qcount + 10, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      taken = code;
+    }
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(taken);
+  } else {
+    item = __builtin_amdgcn_readfirstlane(a.sched[blockIdx.x]);
+  }
+  auto finish = [&]() {
+    if (a.queue != nullptr && tid == 0 && atomicAdd(a.qcount + 9, 1) == a.n_blocks - 1) {
+      for (int i = 0; i < kQueueWords; ++i) __hip_atomic_store(a.qcount + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  if (item == -1) {
+    finish();
+    return;
+  }
+  int piece = -1, s_first = 0, s_end = 0;
+  if (item < -1) {
+    piece = -2 - item;
+    item = __builtin_amdgcn_readfirstlane(a.ptab[4 * piece]);
+    s_first = __builtin_amdgcn_readfirstlane(a.ptab[4 * piece + 1]);
+    s_end = __builtin_amdgcn_readfirstlane(a.ptab[4 * piece + 2]);
+  }
+  const int sub = item % a.subs;
+  const int rest = item / a.subs;
+  const int qt = rest % a.n_tiles;
+  const int bh = rest / a.n_tiles;
+  const int h = bh % a.heads;
 
   // Work-item constants are wave-uniform; readfirstlane keeps them in SGPRs
   // so that the key loop is a scalar (non-divergent) loop.
@@ -182,13 +228,15 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
 
   // ---- key-tile walk ------------------------------------------------------
   const int spt = SWA ? s_nzb : a.V / KB;   // steps per key tile (SWA: per key row)
-  const int nsteps = SWA ? s_nrows * s_nzb : nkv * spt;
+  if (piece < 0) s_end = SWA ? s_nrows * s_nzb : nkv * spt;
+  const int nsteps = s_end - s_first;      // steps of this work group
 
   // Global -> register prefetch of one 32-key block of K and of V.  The rows
   // of the next fetch are looked up (LDS tables) right after the current one
   // is issued, so the lookups never delay a step's global loads.
   Raw8<F32IN> rk[CPT], rv[CPT];
-  int fk_ti = 0, fk_u = 0, fv_ti = 0, fv_u = 0;   // key tile / step-in-tile of the next fetch
+  // key tile / step-in-tile of the next fetch
+  int fk_ti = s_first / spt, fk_u = s_first % spt, fv_ti = fk_ti, fv_u = fk_u;
   int krow[CPT], vrow[CPT];                        // token rows of the next fetch
   auto rows_at = [&](int (&nrow)[CPT], int ti, int u) {
     if constexpr (SWA) {
@@ -414,8 +462,8 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   // zeroed (step 0's P.V of the nonexistent block -1 reads it, with zero
   // probabilities).
   auto begin_walk = [&]() {
-    rows_at(krow, 0, 0);
-    rows_at(vrow, 0, 0);
+    rows_at(krow, fk_ti, fk_u);
+    rows_at(vrow, fv_ti, fv_u);
     fetch(rk, kg, krow, fk_ti, fk_u);
     stash_k(rk, 0);
     uint4 *v1 = reinterpret_cast<uint4 *>(smem + 2 * KST_BYTES + VST_BYTES);
@@ -447,7 +495,7 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     }
   } else {
     qk(0);
-    mask_block(0);
+    mask_block(s_first);
   }
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
@@ -476,7 +524,7 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     if (grp_a) {
       pvmm((s - 1) & 1);
       qk(s & 1);
-      mask_block(s);
+      mask_block(s_first + s);
       mask_swa();
     } else {
       softmax();
@@ -486,7 +534,7 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     } else {
       pvmm((s - 1) & 1);
       qk(s & 1);
-      mask_block(s);
+      mask_block(s_first + s);
       mask_swa();
     }
     if constexpr (SWA) {
@@ -507,6 +555,82 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   if (nsteps & 1) step(nsteps - 1, rk, rv, rk2, rv2);
   if (!grp_a) softmax();
   pvmm((nsteps - 1) & 1);
+
+  // ---- a piece of a split item: publish the partial result (unnormalised
+  // O, reference maxima and row-sum partials); the group's last piece to
+  // arrive combines all of them and finalizes.  Softmax pieces combine
+  // exactly: with M = max of the pieces' reference maxima (exp2 units),
+  // O = sum_p 2^(mb_p - M) O_p and l = sum_p 2^(mb_p - M) l_p.  Pieces may
+  // run on different XCDs, whose L2 caches are not coherent with each
+  // other: the partial result is released with one agent-scope fence (L2
+  // write-back) per work group after every wave's stores have completed,
+  // and the last piece acquires with one agent-scope fence (L2
+  // invalidation) before reading.  One fence per work group rather than one
+  // per wave: each writes back or invalidates the whole L2 of the XCD, which
+  // slows every work group on it.
+  if (piece >= 0) {
+    if constexpr (!SWA && QB == 3 && NW == 8) {
+      constexpr int SLOT = 384 * D + 2 * QB * NT;   // floats per slot (fwd_slot_floats)
+      constexpr int ML = DB * QB * NT * 4;           // float offset of the maxima and row sums
+      __shared__ int last_piece;
+      {
+        float *slot = a.pslot + (size_t)piece * SLOT;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int j = 0; j < QB; ++j) reinterpret_cast<f32x4 *>(slot)[(b * QB + j) * NT + tid] = o[b][j];
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+          slot[ML + j * NT + tid] = mb[j];
+          slot[ML + (QB + j) * NT + tid] = l[j];
+        }
+      }
+      // Every wave's stores have reached its XCD's L2 before the release.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      const int group = __builtin_amdgcn_readfirstlane(a.ptab[4 * piece + 3]);
+      const int first = __builtin_amdgcn_readfirstlane(a.gtab[2 * group]);
+      const int np = __builtin_amdgcn_readfirstlane(a.gtab[2 * group + 1]);
+      if (tid == 0) {
+        __threadfence();                                   // release
+        const bool last = atomicAdd(a.pcount + group, 1) == np - 1;
+        if (last) {
+          __threadfence();                                 // acquire
+          atomicExch(a.pcount + group, 0);                 // ready for the next launch
+        }
+        last_piece = last;
+      }
+      __syncthreads();
+      if (!last_piece) {
+        finish();
+        return;
+      }
+      // Combined in piece order, every partial read back (the last piece's
+      // own included), so that the result does not depend on which piece
+      // arrived last; one query block at a time, which keeps the loads of
+      // one partial block beside the accumulators in registers.
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        float mx = -INFINITY;
+        for (int p = first; p < first + np; ++p) mx = fmaxf(mx, a.pslot[(size_t)p * SLOT + ML + j * NT + tid]);
+        float lj = 0.f;
+        f32x4 oj[DB];
+#pragma unroll
+        for (int b = 0; b < DB; ++b) oj[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int p = first; p < first + np; ++p) {
+          const float *slot = a.pslot + (size_t)p * SLOT;
+          const float f = __builtin_amdgcn_exp2f(slot[ML + j * NT + tid] - mx);
+          lj += f * slot[ML + (QB + j) * NT + tid];
+#pragma unroll
+          for (int b = 0; b < DB; ++b) oj[b] += f * reinterpret_cast<const f32x4 *>(slot)[(b * QB + j) * NT + tid];
+        }
+        mb[j] = mx;
+        l[j] = lj;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) o[b][j] = oj[b];
+      }
+    }
+  }
 
   // ---- finalize: O = O^T / l, stored row-major; optionally the row
   // log-sum-exp, ln(sum_j exp(scale s_j)) = (m * scale * log2(e) + log2(l)) * ln(2).
@@ -535,8 +659,13 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
       }
     }
   }
+  finish();
 }
 
+
+__global__ void zero_kernel(int32_t *p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
 
 template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL, bool SWA = false>
 hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
@@ -572,9 +701,17 @@ hipError_t launch_p(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s) 
 
 }  // namespace
 
+hipError_t launch_zero(int32_t *p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_forward(const FwdArgs &a, int variant, int head_dim, bool f32_in, bool f32_out,
                           hipStream_t stream) {
   if (a.n_blocks <= 0) return hipSuccess;
+  // Split items exist only for the 384-query kernel (not token-wise SWA).
+  if (a.ptab != nullptr && (variant != kTile384 || a.swin != nullptr)) return hipErrorInvalidValue;
   if (variant == kTile384) {
     if (head_dim == 128) return launch_p<128, 3, 8>(a, f32_in, f32_out, stream);
     return launch_p<64, 3, 8>(a, f32_in, f32_out, stream);

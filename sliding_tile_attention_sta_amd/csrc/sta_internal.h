@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <map>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "sta.h"
@@ -18,6 +19,7 @@ enum Variant : int32_t {
 };
 
 constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, blocks dispatched round-robin
+constexpr int kCusPerXcd = 32;    // compute units per XCD (256 in all)
 constexpr int kKeyBlock = 32;     // keys staged in LDS per pipeline step
 constexpr int kMaxTileTokens = 4096;
 
@@ -64,8 +66,29 @@ struct DeviceTables {
   int32_t *sched_dkdv = nullptr;   // backward dK/dV work items in launch order (-1 = idle)
   int32_t *kmask = nullptr;        // partial plans: n_tiles * tile_tokens/32 validity words
   int32_t *swin = nullptr;         // SWA plans: heads*3 token windows
+  int32_t *queue = nullptr;        // dynamic queues: the 8 XCD queues, concatenated
+  int32_t *ptab = nullptr;         // split items: 4 per piece (item, first step, end step, group)
+  int32_t *gtab = nullptr;         // split items: 2 per group (first piece, piece count)
   void *block = nullptr;           // the single allocation holding all of the above
 };
+
+// Scratch of a forward launch of a plan with dynamic queues (the 384-query
+// kernel): 16 int32 queue words (the next free entry of each of the 9
+// queues, then the count of finished work groups and an "every queue is
+// empty" flag; the last work group to finish zeroes them), one int32 arrival
+// counter per split item (the last piece to arrive zeroes it), padded to
+// 256 B, then one partial-result slot per piece.  A slot holds the piece's
+// unnormalised O (QPI x D fp32, in the accumulator layout of the kernel's
+// threads) followed by each thread's reference maxima and row-sum partials
+// (2 x QB x threads fp32).
+constexpr int kQueueWords = 16;
+constexpr long long fwd_slot_floats(int head_dim) {
+  return 384LL * head_dim + 2LL * 3 * 512;
+}
+inline long long fwd_counter_bytes(long long groups) { return (4 * (kQueueWords + groups) + 255) / 256 * 256; }
+inline long long fwd_scratch_bytes(int head_dim, long long groups, long long pieces) {
+  return fwd_counter_bytes(groups) + 4LL * fwd_slot_floats(head_dim) * pieces;
+}
 
 }  // namespace sta
 
@@ -79,7 +102,27 @@ struct sta_plan {
   std::vector<int32_t> win;       // heads*3 effective (clamped) windows
   std::vector<int32_t> kv_off;    // heads*n_tiles + 1
   std::vector<int32_t> kv_idx;    // key tiles per (head, query tile), launch order
-  std::vector<int32_t> sched;     // launch order of work items, -1 = idle
+  std::vector<int32_t> sched;     // launch order of work items, -1 = idle, -2 - p = piece p
+  // Work items split by key range (the forward's last, partial round of
+  // equal-cost items would otherwise leave most compute units idle): piece
+  // p walks steps [ptab[4p+1], ptab[4p+2]) of item ptab[4p] and belongs to
+  // group ptab[4p+3]; group g's pieces are ptab entries gtab[2g] ..
+  // gtab[2g] + gtab[2g+1] - 1.  The last piece of a group to finish merges
+  // the group's partial results (through the launch's scratch).
+  std::vector<int32_t> ptab, gtab;
+  int32_t n_pieces = 0, n_groups = 0;
+  // Dynamic queues (the 384-query forward): per-XCD queues of whole work
+  // items and a ninth queue of pieces, concatenated (queue k at
+  // queue[qoff[k] .. qoff[k+1])).  A work group takes the next entry of its
+  // own XCD's queue with an atomic counter, when that is empty the next
+  // entry of another XCD's, and only when every XCD queue is empty a piece,
+  // so that XCDs that run faster take more of the work and the pieces fill
+  // the end of the launch.  The launch has dyn_blocks work groups (more than
+  // entries); those that find every queue empty exit.  dyn_blocks == 0:
+  // static launch, work group b runs sched[b].
+  std::vector<int32_t> queue;
+  int32_t qoff[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  int32_t dyn_blocks = 0;
   std::vector<int32_t> base_nat, off_nat;
   int64_t pairs = 0;
   int32_t max_nkv = 0;    // longest key-tile list
@@ -113,6 +156,9 @@ struct sta_plan {
 
   mutable std::mutex mu;
   mutable std::map<int, sta::DeviceTables> dev;   // per HIP device ordinal
+  // Forward scratch of plans with split items, one per (device, stream):
+  // launches on one stream run in order, so they can share it.
+  mutable std::map<std::pair<int, void *>, void *> scratch;
 };
 
 namespace sta {

@@ -26,7 +26,24 @@ struct FwdArgs {
   // windows per head (heads*3), extents, query tile sizes, query tile grid.
   const int32_t *swin;
   int32_t T, H, W, tT, tH, tW, gH, gW;
+  // Dynamic queues (NULL: work group b runs sched[b]): the 8 XCD queues and
+  // the piece queue concatenated, queue k at queue[qoff[k] .. qoff[k+1]),
+  // and the launch's queue words (scratch; zero between launches).
+  const int32_t *queue;
+  int32_t qoff[10];
+  int32_t *qcount;
+  // Work items split by key range (entries -2 - p): per piece (item, first
+  // step, end step, group), per group (first piece, pieces), and the
+  // launch's scratch: an arrival counter per group (zero between launches)
+  // and a partial-result slot per piece.  NULL when there are no pieces.
+  const int32_t *ptab;
+  const int32_t *gtab;
+  int32_t *pcount;
+  float *pslot;
 };
+
+// Zero n int32 (a fill kernel, so that the clear can sit in a captured graph).
+hipError_t launch_zero(int32_t *p, int n, hipStream_t stream);
 
 // Launch the forward kernel.  variant: 0 generic, 1 384-query items.
 hipError_t launch_forward(const FwdArgs &a, int variant, int head_dim, bool f32_in, bool f32_out,

@@ -9,8 +9,10 @@
 
 #include <algorithm>
 #include <cstring>
+#include <functional>
 #include <new>
 #include <numeric>
+#include <queue>
 
 #include "sta_internal.h"
 
@@ -24,17 +26,22 @@ inline int window_start(int c, int w, int n) {
   return s;
 }
 
-// Work items in launch order.  Item code ((b * heads + h) * n_tiles + t) *
-// subs + sub; its cost is the length of list (h, t) in off.  Items are
-// sorted by decreasing cost, cut into chunks of consecutive items, and each
-// chunk goes to the XCD with the least accumulated cost.  Blocks are
-// dispatched to XCDs round-robin (block b runs on XCD b % 8), so XCD x's
-// queue is placed at blocks x, x + 8, x + 16, ...  Within an XCD the hardware
-// hands blocks to free compute units in order, which is list scheduling of a
-// decreasing-cost list.  Chunks keep spatially adjacent tiles of one head on
-// the same XCD, whose L2 then serves their overlapping windows.
+// Work items per XCD queue, in launch order.  Item code ((b * heads + h) *
+// n_tiles + t) * subs + sub; its cost is the length of list (h, t) in off.
+// Items are sorted by decreasing cost, cut into chunks of consecutive items,
+// and each chunk goes to the XCD with the least accumulated cost.  Blocks
+// are dispatched to XCDs round-robin (block b runs on XCD b % 8), so XCD x's
+// queue is placed at blocks x, x + 8, x + 16, ...  Within an XCD the
+// hardware hands blocks to free compute units in order, which is list
+// scheduling of a decreasing-cost list.  Chunks keep spatially adjacent
+// tiles of one head on the same XCD, whose L2 then serves their overlapping
+// windows; launches of fewer items than 8 full chunks use smaller chunks,
+// so that every XCD gets work.  The first n_whole items of the order go to
+// the queues; *order receives the whole order.
 template <typename Off>
-std::vector<int32_t> build_schedule(const sta_plan *p, const std::vector<Off> &off, int subs) {
+std::vector<std::vector<int32_t>> build_queues(const sta_plan *p, const std::vector<Off> &off, int subs,
+                                               std::vector<int64_t> *order_out = nullptr,
+                                               int64_t n_whole = -1) {
   const int64_t n_items = (int64_t)p->batch * p->heads * p->n_tiles * subs;
   std::vector<int64_t> order(n_items);
   std::iota(order.begin(), order.end(), 0);
@@ -46,24 +53,122 @@ std::vector<int32_t> build_schedule(const sta_plan *p, const std::vector<Off> &o
   };
   std::stable_sort(order.begin(), order.end(),
                    [&](int64_t a, int64_t b) { return cost(a) > cost(b); });
-
-  const int64_t chunk = 32;  // compute units per XCD
+  if (n_whole < 0) n_whole = n_items;
+  const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(kCusPerXcd, (n_whole + kXcds - 1) / kXcds));
   std::vector<std::vector<int32_t>> queue(kXcds);
   std::vector<int64_t> load(kXcds, 0);
-  for (int64_t i = 0; i < n_items; i += chunk) {
-    int64_t end = std::min(n_items, i + chunk);
+  for (int64_t i = 0; i < n_whole; i += chunk) {
+    int64_t end = std::min(n_whole, i + chunk);
     int64_t c = 0;
     for (int64_t j = i; j < end; ++j) c += cost(order[j]);
     int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
     load[x] += c;
     for (int64_t j = i; j < end; ++j) queue[x].push_back((int32_t)order[j]);
   }
+  if (order_out) order_out->swap(order);
+  return queue;
+}
+
+std::vector<int32_t> interleave(const std::vector<std::vector<int32_t>> &queue) {
   size_t len = 0;
   for (auto &q : queue) len = std::max(len, q.size());
   std::vector<int32_t> sched(len * kXcds, -1);
   for (int x = 0; x < kXcds; ++x)
     for (size_t s = 0; s < queue[x].size(); ++s) sched[s * kXcds + x] = queue[x][s];
   return sched;
+}
+
+constexpr int64_t kMaxPieces = 512;
+constexpr int64_t kMinPieceSteps = 32;
+
+// The forward's dynamic queues (see sta_plan::queue): per-XCD queues of
+// whole work items, and a ninth queue of the pieces of split items, which
+// work groups take only once every XCD queue is empty.  Work items are
+// coarse: one 720p item is about 1/28 of a compute unit's share of the
+// launch, so without pieces the units that drew the last items run up to a
+// whole item after the others.  Splitting (split = true): the last R items
+// of the decreasing-cost order are cut into k pieces of consecutive key
+// steps (steps_per_entry per list entry; boundaries on multiples of align
+// steps), R = 64 (a quarter of the chip's compute units), k = 4, fewer if a
+// piece would walk less than 32 steps or there would be more than 512
+// pieces, and no split at k < 2.  With fewer items than compute units,
+// every item, into the k whose pieces take the fewest rounds of the chip
+// (12x24x24's 144 items: k = 3, two rounds of a third of an item).
+// Measured on MI355X with the 7,200 equal items of the 720p workload: 64
+// items in 4 pieces ran 1 % faster than no split; 128 or 256 items in 4
+// pieces less so, and 256 in 8 slower than no split (every piece adds the
+// write of its partial result, two fences and its share of the merge).
+template <typename Off>
+void build_forward_queues(sta_plan *p, const std::vector<Off> &off, int64_t steps_per_entry, int64_t align,
+                          bool split) {
+  std::vector<int64_t> order;
+  auto whole = build_queues(p, off, p->subs, &order);
+  const int64_t n_items = (int64_t)order.size();
+  auto steps = [&](int64_t code) {
+    const int64_t rest = code / p->subs;
+    const int t = (int)(rest % p->n_tiles), h = (int)((rest / p->n_tiles) % p->heads);
+    return ((int64_t)off[(size_t)h * p->n_tiles + t + 1] - off[(size_t)h * p->n_tiles + t]) * steps_per_entry;
+  };
+  const int64_t units = kXcds * kCusPerXcd;
+  int64_t best_r = 0;
+  int best_k = 1;
+  if (split && n_items > 0) {
+    best_r = n_items < units ? n_items : units / 4;
+    int kmax = (int)std::min<int64_t>(4, kMaxPieces / best_r);
+    for (int64_t i = n_items - best_r; i < n_items; ++i)   // the cheapest items
+      kmax = (int)std::min<int64_t>(kmax, steps(order[i]) / align / std::max<int64_t>(1, kMinPieceSteps / align));
+    if (n_items >= units) {
+      best_k = kmax;
+    } else {
+      // Fewer items than compute units: the k (<= kmax) whose pieces take
+      // the fewest rounds of the chip, ceil(n k / units) / k, ties to the
+      // smaller k.
+      double best = 1.0;
+      for (int k = 2; k <= kmax; ++k) {
+        const double t = (double)((n_items * k + units - 1) / units) / k;
+        if (t < best - 1e-9) { best = t; best_k = k; }
+      }
+    }
+    if (best_k < 2) { best_r = 0; best_k = 1; }
+  }
+  if (best_r > 0) whole = build_queues(p, off, p->subs, nullptr, n_items - best_r);
+  std::vector<int32_t> pieces;
+  for (int64_t i = n_items - best_r; i < n_items; ++i) {
+    const int64_t u = steps(order[i]) / align;
+    const int32_t group = p->n_groups++;
+    p->gtab.push_back(p->n_pieces);
+    p->gtab.push_back(best_k);
+    for (int j = 0; j < best_k; ++j) {
+      p->ptab.push_back((int32_t)order[i]);
+      p->ptab.push_back((int32_t)(u * j / best_k * align));
+      p->ptab.push_back((int32_t)(u * (j + 1) / best_k * align));
+      p->ptab.push_back(group);
+      pieces.push_back(-2 - p->n_pieces++);
+    }
+  }
+  // sched: the XCD queues interleaved, then the pieces.
+  p->sched = interleave(whole);
+  p->sched.insert(p->sched.end(), pieces.begin(), pieces.end());
+  // Launch: 1/16 more work groups per XCD than its queue holds (at least 8
+  // more), so that an XCD whose units run faster can take entries from the
+  // others' queues, plus the pieces spread over the XCDs.
+  size_t len = 0;
+  p->queue.clear();
+  p->qoff[0] = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    p->queue.insert(p->queue.end(), whole[x].begin(), whole[x].end());
+    p->qoff[x + 1] = (int32_t)p->queue.size();
+    len = std::max(len, whole[x].size());
+  }
+  p->queue.insert(p->queue.end(), pieces.begin(), pieces.end());
+  p->qoff[kXcds + 1] = (int32_t)p->queue.size();
+  len += (pieces.size() + kXcds - 1) / kXcds;
+  p->dyn_blocks = (int32_t)(kXcds * (len + std::max<size_t>(8, len / 16)));
+}
+
+template <typename Off>
+std::vector<int32_t> build_schedule(sta_plan *p, const std::vector<Off> &off, int subs) {
+  return interleave(build_queues(p, off, subs));
 }
 
 }  // namespace
@@ -193,7 +298,14 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
         }
       }
     }
-    p->sched = build_schedule(p, p->kv_off, p->subs);
+    // Split items need the 384-query kernel.  Every piece's first key block
+    // must hold an existing key (its reference maximum comes from it): with
+    // partial tiles, pieces start on key-tile boundaries (a tile's first
+    // token always exists).
+    if (p->variant == kTile384)
+      build_forward_queues(p, p->kv_off, p->V / kKeyBlock, p->partial ? p->V / kKeyBlock : 1, true);
+    else
+      p->sched = build_schedule(p, p->kv_off, p->subs);
 
     // Backward: the inverse of the key-tile lists (query tiles whose window
     // holds the key tile), per head, and the two backward schedules.  Launch
@@ -228,11 +340,7 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
       }
     }
     p->bwd_q_waves = p->V % 128 == 0 ? 4 : 1;
-#ifndef STA_DKDV_PAIRS
     p->bwd_k_pairs = p->V % 192 == 0 ? 6 : p->V % 128 == 0 ? 4 : 1;
-#else
-    p->bwd_k_pairs = p->V % (32 * STA_DKDV_PAIRS) == 0 ? STA_DKDV_PAIRS : 1;
-#endif
     p->bwd_q_subs = p->V / (32 * p->bwd_q_waves);
     p->bwd_k_subs = p->V / (32 * p->bwd_k_pairs);
     p->bwd_ok = !p->partial && bwd_lds_bytes(head_dim, p->V, std::max(p->max_nkv, p->max_nq)) <= kMaxLds;
@@ -316,7 +424,10 @@ sta_status build_swa_plan(int batch, int heads, int T, int H, int W, const int t
       const int lt = j / (tile[1] * tile[2]), ly = (j / tile[2]) % tile[1], lz = j % tile[2];
       p->off_nat[j] = (lt * H + ly) * W + lz;
     }
-    p->sched = build_schedule(p, cost_off, p->subs);
+    if (p->variant == kTile384)
+      build_forward_queues(p, cost_off, 1, 1, false);
+    else
+      p->sched = build_schedule(p, cost_off, p->subs);
   } catch (const std::bad_alloc &) {
     delete p;
     return STA_ERR_ALLOC;
@@ -381,6 +492,10 @@ sta_status sta_plan_get_info(const sta_plan *p, sta_plan_info *info) {
   info->bwd_items_dq = (int64_t)p->sched_dq.size();
   info->bwd_items_dkdv = (int64_t)p->sched_dkdv.size();
   info->partial_tiles = p->partial ? 1 : 0;
+  info->split_items = p->n_groups;
+  info->pieces = p->n_pieces;
+  info->scratch_bytes = p->dyn_blocks ? sta::fwd_scratch_bytes(p->D, p->n_groups, p->n_pieces) : 0;
+  info->launch_blocks = p->dyn_blocks ? p->dyn_blocks : (int64_t)p->sched.size();
   return STA_OK;
 }
 
@@ -426,6 +541,21 @@ sta_status sta_plan_schedule_bwd(const sta_plan *p, int which, int32_t *out, int
   *count = (int64_t)s.size();
   if (cap < *count || (!out && *count > 0)) return STA_ERR_ARG;
   if (!s.empty()) std::memcpy(out, s.data(), s.size() * sizeof(int32_t));
+  return STA_OK;
+}
+
+sta_status sta_plan_pieces(const sta_plan *p, int32_t *out, int64_t cap, int64_t *count) {
+  if (!p || !count) return STA_ERR_ARG;
+  *count = (int64_t)p->n_pieces;
+  if (cap < *count || (!out && *count > 0)) return STA_ERR_ARG;
+  for (int32_t i = 0; i < p->n_pieces; ++i) {
+    const int32_t g = p->ptab[4 * i + 3];
+    out[5 * i + 0] = p->ptab[4 * i + 0];
+    out[5 * i + 1] = p->ptab[4 * i + 1];
+    out[5 * i + 2] = p->ptab[4 * i + 2];
+    out[5 * i + 3] = g;
+    out[5 * i + 4] = p->gtab[2 * g + 1];
+  }
   return STA_OK;
 }
 

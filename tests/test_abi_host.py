@@ -10,6 +10,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from oracle import sta_oracle as O
@@ -86,35 +87,76 @@ def test_perm_is_the_tile_major_order():
         assert pos == tile * V + local
 
 
-@pytest.mark.parametrize("name", ["720p", "mixed", "long", "small", "tiny"])
+@pytest.mark.parametrize("name", ["720p", "mixed", "long", "small", "tiny", "720p-exact"])
 def test_schedule_covers_every_item_once_and_balances_xcds(name):
     w = WORKLOADS[name]
-    p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    partial = any(e % t for e, t in zip(w.video, w.tile))
+    p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim, partial_tiles=partial)
     s = p.schedule().numpy()
     info = p.info
     subs = info.tile_tokens // info.queries_per_item
     n_items = w.batch * w.heads * info.n_tiles * subs
-    real = s[s >= 0]
-    assert sorted(real.tolist()) == list(range(n_items))
-    assert (s[s < 0] == -1).all()
-    assert len(s) % 8 == 0
+    # the XCD queues interleaved (entry s * 8 + x of XCD x's queue, -1
+    # padding), then the pieces of split items in the order they are taken
+    n_whole = len(s) - info.pieces
+    assert n_whole % 8 == 0
+    whole, tail = s[:n_whole], s[n_whole:]
+    assert (tail == -2 - np.arange(info.pieces)).all()
+    assert ((whole == -1) | (whole >= 0)).all()
+    pieces = p.pieces().numpy()
+    assert len(pieces) == info.pieces
+    steps = {}
+    for it, a, b, g, n in pieces.tolist():
+        steps.setdefault(it, []).append((a, b, g, n))
+    assert sorted(whole[whole >= 0].tolist() + list(steps)) == list(range(n_items))
+    # the pieces of a split item partition its key steps (on key-tile
+    # boundaries when tiles are partial), and are taken one after another
+    grid = O.tile_grid(w.video, w.tile, partial)
+    V = info.tile_tokens
+    spt = V // 32
+    for it, segs in steps.items():
+        h = (it // subs // info.n_tiles) % w.heads
+        we = O.effective_window(w.windows[h], grid)
+        assert segs[0][0] == 0 and segs[-1][1] == we[0] * we[1] * we[2] * spt
+        assert all(x[1] == y[0] and x[0] < x[1] for x, y in zip(segs, segs[1:]))
+        assert len({g for _, _, g, _ in segs}) == 1 and all(n == len(segs) for *_, n in segs)
+        if partial:
+            assert all(a % spt == 0 for a, *_ in segs)
     # per-XCD cost (block b runs on XCD b % 8): spread within one chunk of items
     cost = {}
-    grid = O.tile_grid(w.video, w.tile)
     for h in range(w.heads):
         we = O.effective_window(w.windows[h], grid)
         cost[h] = we[0] * we[1] * we[2]
     load = [0] * 8
-    for b, code in enumerate(s.tolist()):
+    for b, code in enumerate(whole.tolist()):
         if code >= 0:
-            h = (code // subs // info.n_tiles) % w.heads
-            load[b % 8] += cost[h]
-    if n_items >= 8 * 32:
+            load[b % 8] += cost[(code // subs // info.n_tiles) % w.heads]
+    if n_items - len(steps) >= 8 * 32:
         assert max(load) - min(load) <= 32 * max(cost.values())
     # decreasing cost along each XCD's queue (list scheduling of an LPT order)
     for x in range(8):
-        q = [cost[(c // subs // info.n_tiles) % w.heads] for c in s[x::8].tolist() if c >= 0]
+        q = [cost[(c // subs // info.n_tiles) % w.heads] for c in whole[x::8].tolist() if c >= 0]
         assert q == sorted(q, reverse=True)
+    # split items are the cheapest ones
+    if steps:
+        split_cost = max(cost[(it // subs // info.n_tiles) % w.heads] for it in steps)
+        assert all(cost[(c // subs // info.n_tiles) % w.heads] >= split_cost for c in whole[whole >= 0].tolist())
+    # the launch has more work groups than entries (dynamic queues) or exactly sched
+    if info.kernel_variant == 1:
+        assert info.launch_blocks >= len(s) and info.scratch_bytes > 0
+    else:
+        assert info.launch_blocks == len(s) and info.scratch_bytes == 0
+
+
+def test_tail_is_split_only_where_it_pays():
+    """Equal-cost items whose count is not a multiple of the chip's 256
+    compute units get their tail split; the mixed-window workload, whose
+    decreasing-cost order ends in one-tile items, does not."""
+    for name, split in (("720p", True), ("long", True), ("small", True), ("mixed", False), ("tiny", False)):
+        w = WORKLOADS[name]
+        i = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim).info
+        assert (i.pieces > 0) == split, name
+        assert i.pieces <= 512
 
 
 def _create(*args):
