@@ -226,6 +226,25 @@ sta_status sta_forward_plan_lse(const sta_plan *plan, const void *q, const void 
                                 void *out, float *lse, float scale, sta_dtype in_dtype,
                                 sta_dtype out_dtype, sta_layout layout, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as sta_forward_plan / sta_forward_plan_lse (lse may be NULL), with
+ * no hipMalloc, hipFree or other allocating call.  Its work queues, arrival
+ * counters and partial results use a fixed scratch array of 64 MiB that
+ * each device holds while the library is loaded; the call clears the
+ * counters with a small kernel on stream before the forward kernel.  Every
+ * call on one device shares that device's array, so calls that overlap on
+ * one device (different streams, host threads) race: serialise them.
+ * The plan's tables must already be on the current device (any earlier
+ * allocating call with the plan there -- sta_forward_plan, _lse,
+ * sta_backward_plan, sta_tile_reorder -- uploads them).
+ * Errors: as sta_forward_plan; STA_ERR_UNSUPPORTED if the plan's tables are
+ * not on the device yet or its scratch (sta_plan_info.scratch_bytes) is
+ * larger than 64 MiB. */
+sta_status sta_forward_plan_noalloc(const sta_plan *plan, const void *q, const void *k, const void *v,
+                                    void *out, float *lse, float scale, sta_dtype in_dtype,
+                                    sta_dtype out_dtype, sta_layout layout, void *stream);
+
 /* STA backward: gradients of <out, dout> with respect to q, k and v, where
  * out is STA's output for (q, k, v).  Defined by the chain rule of the
  * forward (the pages fine-tune through the operator; index page, Abstract,

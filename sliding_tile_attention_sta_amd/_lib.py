@@ -57,6 +57,7 @@ SIGNATURES = {
     "sta_tile_unreorder": (_I, [_P, _P, _P, _I, _P]),
     "sta_forward_plan": (_I, [_P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I, _P]),
     "sta_forward_plan_lse": (_I, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I, _P]),
+    "sta_forward_plan_noalloc": (_I, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I, _P]),
     "sta_backward_plan": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _I, _I, _I,
                                _I, _P]),
     "sta_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _IP, _IP, _I, ctypes.c_float,

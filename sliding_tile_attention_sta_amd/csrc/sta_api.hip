@@ -77,6 +77,45 @@ sta_status device_tables(const sta_plan *p, DeviceTables *out) {
   return STA_OK;
 }
 
+// The plan's tables on the current device if they were uploaded before
+// (no allocation); STA_ERR_UNSUPPORTED if not.
+sta_status existing_device_tables(const sta_plan *p, DeviceTables *out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return STA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(p->mu);
+  auto it = p->dev.find(dev);
+  if (it == p->dev.end()) return STA_ERR_UNSUPPORTED;
+  *out = it->second;
+  return STA_OK;
+}
+
+// Scratch of sta_forward_plan_noalloc: a fixed array in device memory that
+// each device holds while the library is loaded, shared by every such call
+// on that device.  64 MiB: the queue words and arrival counters of any plan
+// and the partial-result slots of up to about 320 pieces at head_dim 128
+// (the 720p and 60x48x80 workloads use 256).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __attribute__((aligned(256))) int32_t scratch[kStaticScratchBytes / 4];
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void *g_static_ptr[kMaxDevices] = {};   // device address of scratch, per device
+
+// The device address of scratch on the current device.  Looked up once per
+// device (hipGetSymbolAddress, with that device current); in host code the
+// array's name is only a stand-in, never a device address.
+sta_status static_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return STA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (g_static_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return STA_ERR_HIP;
+    g_static_ptr[dev] = ptr;
+  }
+  *out = g_static_ptr[dev];
+  return STA_OK;
+}
+
 // The forward scratch of a plan with dynamic queues on the current device,
 // for launches on `stream` (allocated on first use; its counters are
 // cleared once, in stream order, and every launch leaves them zero).
@@ -186,8 +225,12 @@ sta_status sta_tile_unreorder(const sta_plan *plan, const void *in, void *out, s
 namespace sta {
 namespace {
 
+// no_alloc: use the plan's device tables only if they exist, and the
+// library's static scratch (cleared by a kernel at every call) instead of a
+// per-stream allocation.
 sta_status forward(const sta_plan *p, const void *q, const void *k, const void *v, void *out, float *lse,
-                   float scale, sta_dtype in_dtype, sta_dtype out_dtype, sta_layout layout, void *stream) {
+                   float scale, sta_dtype in_dtype, sta_dtype out_dtype, sta_layout layout, void *stream,
+                   bool no_alloc = false) {
   if (!p || !q || !k || !v || !out) return STA_ERR_ARG;
   if (!sta::valid_dtype(in_dtype) || !sta::valid_dtype(out_dtype)) return STA_ERR_ARG;
   if (layout != STA_LAYOUT_NATURAL && layout != STA_LAYOUT_TILE_MAJOR) return STA_ERR_ARG;
@@ -204,11 +247,25 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
       return STA_ERR_ARG;
   }
   sta::DeviceTables t;
-  sta_status st = sta::device_tables(p, &t);
-  if (st != STA_OK) return st;
   void *scratch = nullptr;
-  st = forward_scratch(p, stream, &scratch);
-  if (st != STA_OK) return st;
+  if (no_alloc) {
+    const long long need = p->dyn_blocks ? fwd_scratch_bytes(p->D, p->n_groups, p->n_pieces) : 0;
+    if (need > (long long)kStaticScratchBytes) return STA_ERR_UNSUPPORTED;
+    sta_status st = existing_device_tables(p, &t);
+    if (st != STA_OK) return st;
+    if (p->dyn_blocks) {
+      st = static_scratch(&scratch);
+      if (st != STA_OK) return st;
+      if (launch_zero(static_cast<int32_t *>(scratch), kQueueWords + p->n_groups, static_cast<hipStream_t>(stream)) !=
+          hipSuccess)
+        return STA_ERR_HIP;
+    }
+  } else {
+    sta_status st = sta::device_tables(p, &t);
+    if (st != STA_OK) return st;
+    st = forward_scratch(p, stream, &scratch);
+    if (st != STA_OK) return st;
+  }
   sta::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = out;
   a.sched = t.sched;
@@ -323,6 +380,12 @@ sta_status sta_forward_plan_lse(const sta_plan *p, const void *q, const void *k,
                                 sta_dtype out_dtype, sta_layout layout, void *stream) {
   if (!lse) return STA_ERR_ARG;
   return sta::forward(p, q, k, v, out, lse, scale, in_dtype, out_dtype, layout, stream);
+}
+
+sta_status sta_forward_plan_noalloc(const sta_plan *p, const void *q, const void *k, const void *v,
+                                    void *out, float *lse, float scale, sta_dtype in_dtype,
+                                    sta_dtype out_dtype, sta_layout layout, void *stream) {
+  return sta::forward(p, q, k, v, out, lse, scale, in_dtype, out_dtype, layout, stream, true);
 }
 
 sta_status sta_backward_plan(const sta_plan *p, const void *q, const void *k, const void *v,
