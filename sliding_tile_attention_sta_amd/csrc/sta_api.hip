@@ -282,6 +282,12 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   a.n_blocks = (int32_t)p->sched.size();
   a.max_nkv = p->max_nkv;
   a.lse = lse;
+  // Per-step addressing of K and V: whole tiles, blocks that are a first row
+  // plus per-position offsets, a step table that fits in LDS beside the
+  // stages, and tensors of one (batch, head) below 2 GiB (32-bit offsets).
+  a.sep = !p->partial && !p->swa && (layout == STA_LAYOUT_TILE_MAJOR || p->sep_nat) &&
+          fwd_lds_bytes(p->D, p->V, p->max_nkv) + fwd_lds_step_bytes(p->V, p->max_nkv) <= kMaxLds &&
+          p->N * p->D * (long long)dtype_bytes(in_dtype) < (1LL << 31);
   a.kmask = reinterpret_cast<const uint32_t *>(t.kmask);
   a.swin = t.swin;
   a.T = p->T; a.H = p->H; a.W = p->W;

@@ -92,7 +92,7 @@ __device__ __forceinline__ int tok_start(int x, int w, int e) {
 }
 
 // D: head dim.  QB: 16-query blocks per wave.  NW: waves per group.
-template <int D, int QB, int NW, bool F32IN, bool F32OUT, bool PARTIAL, bool SWA = false>
+template <int D, int QB, int NW, bool F32IN, bool F32OUT, bool PARTIAL, bool SWA = false, bool SEP = false>
 __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QPI = 16 * QB * NW;               // queries per work item
@@ -206,6 +206,14 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     for (int i = tid; i < nkv * words; i += NT)
       mw_l[i] = a.kmask[(size_t)a.kv_idx[kv0 + i / words] * words + i % words];
   }
+  // SEP: the byte offset of the first key row of every 32-key block of the
+  // walk (the rows of a block are that row plus a fixed offset per position).
+  int *stp_l = reinterpret_cast<int *>(kvb_l + a.max_nkv);
+  if constexpr (SEP) {
+    const int spb = a.V / KB;
+    for (int i = tid; i < nkv * spb; i += NT)
+      stp_l[i] = (a.base[a.kv_idx[kv0 + i / spb]] + a.off[(i % spb) * KB]) * (D * EB);
+  }
 
   const char *qg = reinterpret_cast<const char *>(a.q) + (size_t)bh * a.N * D * EB;
   const char *kg = reinterpret_cast<const char *>(a.k) + (size_t)bh * a.N * D * EB;
@@ -263,7 +271,42 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
       if constexpr (PARTIAL) nrow[i] = nrow[i] < a.N ? nrow[i] : (int)a.N - 1;
     }
   };
+  // SEP: a 32-key block is read with buffer loads at a per-lane constant
+  // byte offset (the chunk's position in the block) plus the block's first
+  // row from the step table, looked up one fetch ahead; fetches past the
+  // walk re-read its last block.
+  int voff[CPT];
+  const int nwalk = nkv * spt;
+  if constexpr (SEP) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      voff[i] = (off_l[(c / (D / 8)) % KB] - off_l[0]) * (D * EB) + (c % (D / 8)) * 8 * EB;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(kg), (short)0, SEP ? (int)(a.N * D * EB) : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(vg), (short)0, SEP ? (int)(a.N * D * EB) : 0, 0x00020000);
   auto fetch = [&](Raw8<F32IN>(&dst)[CPT], const char *src, int (&nrow)[CPT], int &ti, int &u) {
+    if constexpr (SEP) {
+      // nrow[0] holds the byte offset of the block to fetch, ti its step
+      const __amdgpu_buffer_rsrc_t rs = src == kg ? krs : vrs;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * NT;
+        if (CHUNKS < NT && c >= CHUNKS) break;
+        if constexpr (F32IN) {
+          dst[i].x = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + nrow[0], 0, 0));
+          dst[i].y = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + nrow[0] + 16, 0, 0));
+        } else {
+          dst[i].x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + nrow[0], 0, 0));
+        }
+      }
+      ++ti;
+      nrow[0] = stp_l[ti < nwalk ? ti : nwalk - 1];
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
@@ -462,8 +505,14 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   // zeroed (step 0's P.V of the nonexistent block -1 reads it, with zero
   // probabilities).
   auto begin_walk = [&]() {
-    rows_at(krow, fk_ti, fk_u);
-    rows_at(vrow, fv_ti, fv_u);
+    if constexpr (SEP) {
+      // the step counters live in fk_ti / fv_ti, the table offsets in krow[0] / vrow[0]
+      fk_ti = fv_ti = s_first;
+      krow[0] = vrow[0] = stp_l[s_first];
+    } else {
+      rows_at(krow, fk_ti, fk_u);
+      rows_at(vrow, fv_ti, fv_u);
+    }
     fetch(rk, kg, krow, fk_ti, fk_u);
     stash_k(rk, 0);
     uint4 *v1 = reinterpret_cast<uint4 *>(smem + 2 * KST_BYTES + VST_BYTES);
@@ -667,10 +716,11 @@ __global__ void zero_kernel(int32_t *p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
-template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL, bool SWA = false>
+template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL, bool SWA = false, bool SEP = false>
 hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
-  auto kern = sta_fwd_kernel<D, QB, NW, FI, FO, PARTIAL, SWA>;
-  const size_t lds = (size_t)fwd_lds_bytes(D, a.V, a.max_nkv) + (PARTIAL ? 4 * (size_t)a.max_nkv * (a.V / KB) : 0);
+  auto kern = sta_fwd_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, SEP>;
+  const size_t lds = (size_t)fwd_lds_bytes(D, a.V, a.max_nkv) +
+                     (PARTIAL || SEP ? (size_t)fwd_lds_step_bytes(a.V, a.max_nkv) : 0);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -681,10 +731,13 @@ hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int QB, int NW, bool P>
+template <int D, int QB, int NW, bool P, bool SEP = false>
 hipError_t launch_io(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s) {
-  if (f32_in) return f32_out ? launch_one<D, QB, NW, true, true, P>(a, s) : launch_one<D, QB, NW, true, false, P>(a, s);
-  return f32_out ? launch_one<D, QB, NW, false, true, P>(a, s) : launch_one<D, QB, NW, false, false, P>(a, s);
+  if (f32_in)
+    return f32_out ? launch_one<D, QB, NW, true, true, P, false, SEP>(a, s)
+                   : launch_one<D, QB, NW, true, false, P, false, SEP>(a, s);
+  return f32_out ? launch_one<D, QB, NW, false, true, P, false, SEP>(a, s)
+                 : launch_one<D, QB, NW, false, false, P, false, SEP>(a, s);
 }
 
 template <int D, int QB, int NW>
@@ -696,6 +749,7 @@ hipError_t launch_p(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s) 
                    : launch_one<D, QB, NW, false, false, false, true>(a, s);
   }
   if (a.kmask != nullptr) return launch_io<D, QB, NW, true>(a, f32_in, f32_out, s);
+  if (a.sep) return launch_io<D, QB, NW, false, true>(a, f32_in, f32_out, s);
   return launch_io<D, QB, NW, false>(a, f32_in, f32_out, s);
 }
 

@@ -38,6 +38,12 @@ constexpr long long fwd_lds_bytes(int head_dim, long long tile_tokens, long long
   return 2LL * kKeyBlock * (fwd_kstride(head_dim) + fwd_vstride(head_dim)) +
          4LL * (tile_tokens + max_nkv);
 }
+// Added to it: one word per 32-key step of the longest walk (the steps'
+// token-validity words with partial tiles, or the byte offsets of the
+// steps' first key rows when K and V are addressed per step).
+constexpr long long fwd_lds_step_bytes(long long tile_tokens, long long max_nkv) {
+  return 4LL * max_nkv * (tile_tokens / kKeyBlock);
+}
 constexpr long long kMaxLds = 160 * 1024;
 
 // The backward kernels stream blocks of 32 tokens (keys for dQ, queries for
@@ -97,6 +103,12 @@ struct sta_plan {
   int32_t tile[3] = {0, 0, 0};
   int32_t grid[3] = {0, 0, 0};
   int32_t V = 0;          // tokens per tile
+  // Rows of every 32-key block in the natural layout are the block's first
+  // row plus a fixed offset per position in the block (true for tiles whose
+  // blocks are whole (t, y) runs of z, e.g. 6x8x8; the tile-major layout
+  // always is): the forward then addresses K and V with one per-lane
+  // constant and one uniform offset per step.
+  bool sep_nat = false;
   int32_t n_tiles = 0;
   int64_t N = 0;          // tokens
   std::vector<int32_t> win;       // heads*3 effective (clamped) windows

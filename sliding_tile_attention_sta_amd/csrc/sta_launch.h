@@ -21,6 +21,8 @@ struct FwdArgs {
   int32_t n_blocks;        // length of sched
   int32_t max_nkv;         // longest key-tile list of any (head, query tile)
   float *lse;              // NULL, or [batch, heads, N] row log-sum-exp (natural log)
+  int32_t sep;             // rows of a 32-key block = its first row + a per-position offset
+                           // (and the step table fits in LDS): per-step addressing
   const uint32_t *kmask;   // NULL (whole tiles), or per tile V/32 words of token validity
   // Token-wise SWA plans only (swin == NULL otherwise): clamped token
   // windows per head (heads*3), extents, query tile sizes, query tile grid.

@@ -211,7 +211,7 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
       pairs += n_tiles * vol;
     }
     if (pairs > (int64_t)INT32_MAX) return STA_ERR_UNSUPPORTED;
-    if (fwd_lds_bytes(head_dim, V64, longest) + (partial ? 4LL * longest * (V64 / kKeyBlock) : 0) > kMaxLds)
+    if (fwd_lds_bytes(head_dim, V64, longest) + (partial ? fwd_lds_step_bytes(V64, longest) : 0) > kMaxLds)
       return STA_ERR_UNSUPPORTED;
   }
 
@@ -267,7 +267,7 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
       p->max_nkv = std::max(p->max_nkv, p->kv_off[i + 1] - p->kv_off[i]);
     // The forward kernel keeps two K and two V stages of 32 keys plus the
     // tile-local row offsets and the item's key-tile rows in LDS (160 KiB).
-    if (fwd_lds_bytes(head_dim, p->V, p->max_nkv) + (p->partial ? 4LL * p->max_nkv * (p->V / kKeyBlock) : 0) >
+    if (fwd_lds_bytes(head_dim, p->V, p->max_nkv) + (p->partial ? fwd_lds_step_bytes(p->V, p->max_nkv) : 0) >
         kMaxLds) {
       delete p;
       return STA_ERR_UNSUPPORTED;
@@ -284,6 +284,10 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
       const int lt = j / (tile[1] * tile[2]), ly = (j / tile[2]) % tile[1], lz = j % tile[2];
       p->off_nat[j] = (lt * H + ly) * W + lz;
     }
+    p->sep_nat = true;
+    for (int j = 0; j < p->V; ++j)
+      if (p->off_nat[j] - p->off_nat[j / kKeyBlock * kKeyBlock] != p->off_nat[j % kKeyBlock] - p->off_nat[0])
+        p->sep_nat = false;
     if (p->partial) {
       // Token validity per tile; with partial tiles base + off can name a
       // row past the tile's edge (or past the tensor), which the kernel
