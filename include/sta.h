@@ -84,7 +84,8 @@ typedef struct {
   int32_t swa;              /* 1 for a token-wise sliding-window plan (sta_swa_plan_create) */
   int32_t split_items;      /* forward work items split by key range (0 = none) */
   int32_t pieces;           /* launched pieces of those items */
-  int64_t scratch_bytes;    /* device scratch a forward launch of this plan uses (0 = none) */
+  int64_t scratch_bytes;    /* device scratch a forward launch of this plan uses (queue and
+                               arrival counters, fix-up marks, partial results of pieces) */
   int64_t launch_blocks;    /* work groups of one forward launch */
 } sta_plan_info;
 

@@ -30,11 +30,14 @@ HIP_SOURCES = ["sta_api.hip", "sta_forward.hip", "sta_backward.hip", "sta_reorde
 # Its instructions are scheduled with the AMDGPU-specific register-pressure
 # trackers and without the scheduler's clustered low-occupancy rescheduling
 # stage (measured 0.3-0.5 % and a further 0.5-1 % faster on the 720p
-# forward, same 236 VGPRs; the backward kernels ran 0.6 % slower with the
-# trackers and keep the default).
+# forward, same VGPR count; the backward kernels ran 0.6 % slower with the
+# trackers and keep the default).  Loop heads start on 64-byte boundaries, so
+# that the key loop's placement does not depend on the size of the code
+# before it (unaligned, the same loop measured up to 0.6 % slower).
 HIP_EXTRA = {"sta_forward.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
                                  "-mllvm", "-amdgpu-use-amdgpu-trackers",
-                                 "-mllvm", "-amdgpu-disable-clustered-low-occupancy-reschedule"]}
+                                 "-mllvm", "-amdgpu-disable-clustered-low-occupancy-reschedule",
+                                 "-falign-loops=64"]}
 CXX_SOURCES = ["sta_plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")

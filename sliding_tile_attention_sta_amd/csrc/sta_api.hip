@@ -121,7 +121,7 @@ sta_status static_scratch(void **out) {
 // cleared once, in stream order, and every launch leaves them zero).
 sta_status forward_scratch(const sta_plan *p, void *stream, void **out) {
   *out = nullptr;
-  if (p->dyn_blocks == 0) return STA_OK;
+
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return STA_ERR_HIP;
   std::lock_guard<std::mutex> lock(p->mu);
@@ -132,10 +132,10 @@ sta_status forward_scratch(const sta_plan *p, void *stream, void **out) {
     return STA_OK;
   }
   void *buf = nullptr;
-  if (hipMalloc(&buf, (size_t)fwd_scratch_bytes(p->D, p->n_groups, p->n_pieces)) != hipSuccess)
+  if (hipMalloc(&buf, (size_t)p->fwd_scratch()) != hipSuccess)
     return STA_ERR_ALLOC;
-  if (launch_zero(static_cast<int32_t *>(buf), kQueueWords + p->n_groups, static_cast<hipStream_t>(stream)) !=
-      hipSuccess) {
+  if (launch_zero(static_cast<int32_t *>(buf), (int)fwd_zero_words(p->n_groups, p->items()),
+                  static_cast<hipStream_t>(stream)) != hipSuccess) {
     (void)hipFree(buf);
     return STA_ERR_HIP;
   }
@@ -249,17 +249,14 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   sta::DeviceTables t;
   void *scratch = nullptr;
   if (no_alloc) {
-    const long long need = p->dyn_blocks ? fwd_scratch_bytes(p->D, p->n_groups, p->n_pieces) : 0;
-    if (need > (long long)kStaticScratchBytes) return STA_ERR_UNSUPPORTED;
+    if (p->fwd_scratch() > (long long)kStaticScratchBytes) return STA_ERR_UNSUPPORTED;
     sta_status st = existing_device_tables(p, &t);
     if (st != STA_OK) return st;
-    if (p->dyn_blocks) {
-      st = static_scratch(&scratch);
-      if (st != STA_OK) return st;
-      if (launch_zero(static_cast<int32_t *>(scratch), kQueueWords + p->n_groups, static_cast<hipStream_t>(stream)) !=
-          hipSuccess)
-        return STA_ERR_HIP;
-    }
+    st = static_scratch(&scratch);
+    if (st != STA_OK) return st;
+    if (launch_zero(static_cast<int32_t *>(scratch), (int)fwd_zero_words(p->n_groups, p->items()),
+                    static_cast<hipStream_t>(stream)) != hipSuccess)
+      return STA_ERR_HIP;
   } else {
     sta_status st = sta::device_tables(p, &t);
     if (st != STA_OK) return st;
@@ -299,10 +296,12 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   if (p->dyn_blocks) a.n_blocks = p->dyn_blocks;
   a.ptab = t.ptab;
   a.gtab = t.gtab;
-  a.pcount = scratch ? a.qcount + kQueueWords : nullptr;
-  a.pslot = scratch && p->n_pieces
-                ? reinterpret_cast<float *>(static_cast<char *>(scratch) + fwd_counter_bytes(p->n_groups))
-                : nullptr;
+  a.pcount = a.qcount + kQueueWords;
+  a.fbits = reinterpret_cast<unsigned *>(a.pcount + p->n_groups);
+  a.flist = a.qcount + fwd_zero_words(p->n_groups, p->items());
+  a.pslot = p->n_pieces ? reinterpret_cast<float *>(static_cast<char *>(scratch) +
+                                                    fwd_counter_bytes(p->n_groups, p->items()))
+                        : nullptr;
   hipError_t e = sta::launch_forward(a, p->variant, p->D, in_dtype == STA_F32, out_dtype == STA_F32,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? STA_OK : STA_ERR_HIP;

@@ -51,10 +51,12 @@ __device__ __forceinline__ uint4 as_bf16(const Raw8<F32> &r) {
   }
 }
 
-// As fp16 for the P.V product.  bf16 values inside the fp16 range convert
-// exactly; fp32 inputs are rounded to nearest even.  The caller keeps V within
-// the fp16 range (|v| <= 65504); a saturating clamp here sits on the step's
-// critical path and costs about 3 % on MI355X.
+// As fp16 for the P.V product: fp32 inputs, and bf16 values below fp16's
+// normal range (|v| < 2^-14, kept with fewer bits or flushed), are rounded
+// to nearest even; other bf16 values inside the fp16 range convert exactly.
+// Larger magnitudes (|v| > 65504) become infinities: the forward kernel
+// detects those from its output and redoes the work with V scaled
+// (as_f16_scaled).
 template <bool F32>
 __device__ __forceinline__ uint4 as_f16(const Raw8<F32> &r) {
   f16x8 h;
@@ -69,6 +71,39 @@ __device__ __forceinline__ uint4 as_f16(const Raw8<F32> &r) {
     for (int i = 0; i < 8; ++i) h[i] = (_Float16)((float)b[i]);
   }
   return __builtin_bit_cast(uint4, h);
+}
+
+// As as_f16, after multiplying by a power of two (exact unless the product
+// leaves fp32's normal range).
+template <bool F32>
+__device__ __forceinline__ uint4 as_f16_scaled(const Raw8<F32> &r, float scale) {
+  f16x8 h;
+  if constexpr (F32) {
+    h[0] = (_Float16)(r.x.x * scale); h[1] = (_Float16)(r.x.y * scale);
+    h[2] = (_Float16)(r.x.z * scale); h[3] = (_Float16)(r.x.w * scale);
+    h[4] = (_Float16)(r.y.x * scale); h[5] = (_Float16)(r.y.y * scale);
+    h[6] = (_Float16)(r.y.z * scale); h[7] = (_Float16)(r.y.w * scale);
+  } else {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, r.x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (_Float16)((float)b[i] * scale);
+  }
+  return __builtin_bit_cast(uint4, h);
+}
+
+// Largest magnitude of the 8 elements.
+template <bool F32>
+__device__ __forceinline__ float max_abs8(const Raw8<F32> &r) {
+  if constexpr (F32) {
+    return fmaxf(fmaxf(fmaxf(fabsf(r.x.x), fabsf(r.x.y)), fmaxf(fabsf(r.x.z), fabsf(r.x.w))),
+                 fmaxf(fmaxf(fabsf(r.y.x), fabsf(r.y.y)), fmaxf(fabsf(r.y.z), fabsf(r.y.w))));
+  } else {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, r.x);
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf((float)b[i]));
+    return m;
+  }
 }
 
 }  // namespace sta

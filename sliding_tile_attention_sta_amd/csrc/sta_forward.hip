@@ -59,6 +59,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "sta_device.h"
 #include "sta_internal.h"
@@ -92,7 +93,8 @@ __device__ __forceinline__ int tok_start(int x, int w, int e) {
 }
 
 // D: head dim.  QB: 16-query blocks per wave.  NW: waves per group.
-template <int D, int QB, int NW, bool F32IN, bool F32OUT, bool PARTIAL, bool SWA = false, bool SEP = false>
+template <int D, int QB, int NW, bool F32IN, bool F32OUT, bool PARTIAL, bool SWA = false, bool SEP = false,
+          bool FIXUP = false>
 __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QPI = 16 * QB * NW;               // queries per work item
@@ -127,8 +129,11 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   // The item is uniform: readfirstlane keeps it and everything derived from
   // it in SGPRs.  A piece of a split item walks steps [s_first, s_end) of
   // the item's key blocks.
-  int item;
-  if (a.queue != nullptr) {
+  __shared__ int last_piece;      // a split item's piece: the last one to arrive
+  __shared__ unsigned vmax_bits;  // FIXUP: largest |v| of the item's keys
+  int item = -1;
+  if constexpr (FIXUP) {
+  } else if (a.queue != nullptr) {
     __shared__ int taken;
     if (tid == 0) {
       int code = -1;
@@ -154,12 +159,37 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   }
   auto finish = [&]() {
     if (a.queue != nullptr && tid == 0 && atomicAdd(a.qcount + 9, 1) == a.n_blocks - 1) {
-      for (int i = 0; i < kQueueWords; ++i) __hip_atomic_store(a.qcount + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // queue counters, finished work groups, empty flag (the marked items'
+      // count is the fix-up kernel's to read and reset)
+      for (int i = 0; i < 11; ++i) __hip_atomic_store(a.qcount + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
-  if (item == -1) {
+  if (!FIXUP && item == -1) {
     finish();
     return;
+  }
+  // FIXUP: the items the forward marked (V beyond fp16's range, see the
+  // check after the walk), taken in turn by the work groups and redone with
+  // V scaled; the last work group out clears the marks for the next launch.
+  int nbad = 0, fix_k = blockIdx.x;
+  if constexpr (FIXUP) {
+    nbad = __builtin_amdgcn_readfirstlane(__hip_atomic_load(a.qcount + 11, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT));
+    if (nbad == 0) return;
+  }
+next_item:
+  if constexpr (FIXUP) {
+    if (fix_k >= nbad) {
+      if (tid == 0 && atomicAdd(a.qcount + 12, 1) == (int)gridDim.x - 1) {
+        for (int k = 0; k < nbad; ++k)
+          __hip_atomic_store(a.fbits + (a.flist[k] >> 5), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.qcount + 11, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.qcount + 12, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return;
+    }
+    item = __builtin_amdgcn_readfirstlane(a.flist[fix_k]);
+    fix_k += gridDim.x;
   }
   int piece = -1, s_first = 0, s_end = 0;
   if (item < -1) {
@@ -325,13 +355,18 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
       *reinterpret_cast<uint4 *>(ks + (c / (D / 8)) * KSTR + (c % (D / 8)) * 16) = as_bf16<F32IN>(src[i]);
     }
   };
+  // V is stored as fp16 for the P.V product.  vscale == 1: plain
+  // conversion; otherwise (SCALED) V is multiplied by vscale (a power of
+  // two) first.
+  float vscale = 1.f;
   auto stash_v = [&](const Raw8<F32IN>(&src)[CPT], int stage) {
     char *vs = smem + 2 * KST_BYTES + stage * VST_BYTES;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (CHUNKS < NT && c >= CHUNKS) break;
-      *reinterpret_cast<uint4 *>(vs + (c / (D / 8)) * VSTR + (c % (D / 8)) * 16) = as_f16<F32IN>(src[i]);
+      *reinterpret_cast<uint4 *>(vs + (c / (D / 8)) * VSTR + (c % (D / 8)) * 16) =
+          FIXUP ? as_f16_scaled<F32IN>(src[i], vscale) : as_f16<F32IN>(src[i]);
     }
   };
 
@@ -505,6 +540,9 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   // zeroed (step 0's P.V of the nonexistent block -1 reads it, with zero
   // probabilities).
   auto begin_walk = [&]() {
+    fk_ti = fv_ti = s_first / spt;
+    fk_u = fv_u = s_first % spt;
+    if constexpr (SWA) { cur_row = 0; cur_u = 0; }
     if constexpr (SEP) {
       // the step counters live in fk_ti / fv_ti, the table offsets in krow[0] / vrow[0]
       fk_ti = fv_ti = s_first;
@@ -524,6 +562,53 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
   };
 
+  // fp16 holds |v| <= 65504.  A V entry beyond it becomes an infinity in
+  // the P.V operand, which makes the work group's O non-finite; with finite
+  // inputs nothing else can (the probabilities are fp16 too, and a row sum
+  // that overflows is repaired before it is used, so |O| <= 65504^2 times
+  // the keys' count).  The check runs on the accumulators' bits as
+  // integers: their exponent field is all ones only for an infinity or a
+  // NaN (a floating-point test would be folded away, since this file is
+  // built without NaN semantics).  A wave that finds one marks its item
+  // (once per item, through a bit set), and the launch's second kernel
+  // (FIXUP) redoes every marked item with V multiplied by 2^-e, e chosen
+  // from the largest |v| of the item's keys, and O by 2^e: exact scalings,
+  // so only fp16's range moves (entries below 2^(e-25) of the largest round
+  // to zero, far below the output's precision).  No barrier is added to the
+  // common path.
+  float oscale = 1.f;
+  if constexpr (FIXUP) {
+    if (tid == 0) vmax_bits = 0u;
+    fv_ti = s_first / spt;
+    fv_u = s_first % spt;
+    if constexpr (SEP) {
+      fv_ti = s_first;
+      vrow[0] = stp_l[s_first];
+    } else {
+      rows_at(vrow, fv_ti, fv_u);
+    }
+    float vm = 0.f;
+    for (int s = 0; s < nsteps; ++s) {
+      fetch(rv, vg, vrow, fv_ti, fv_u);
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * NT;
+        if (CHUNKS < NT && c >= CHUNKS) break;
+        vm = fmaxf(vm, max_abs8<F32IN>(rv[i]));
+      }
+    }
+    __syncthreads();
+    atomicMax(&vmax_bits, __float_as_uint(vm));
+    __syncthreads();
+    int ex = 0;
+    (void)frexpf(__uint_as_float(vmax_bits), &ex);   // largest |v| < 2^ex
+    const int e = ex > 15 ? ex - 15 : 0;              // largest |v| * 2^-e < 2^15
+    vscale = ldexpf(1.f, -e);
+    oscale = ldexpf(1.f, e);
+  }
+
+  // The walk: the initial reference max, then every key block of this
+  // work group's steps.
   begin_walk();
   // Initial reference max: each row's max over the first key block (which
   // always holds an existing key: a tile's first token is inside the video).
@@ -604,6 +689,19 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   if (nsteps & 1) step(nsteps - 1, rk, rv, rk2, rv2);
   if (!grp_a) softmax();
   pvmm((nsteps - 1) & 1);
+  if constexpr (!FIXUP) {
+    unsigned top = 0u;   // largest (bits << 1): exponent field all ones iff >= 0xff000000
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int j = 0; j < QB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) top = max(top, __float_as_uint(o[b][j][r]) << 1);
+    if (__builtin_amdgcn_ballot_w64(top >= 0xff000000u) != 0 && lane == 0) {
+      const unsigned bit = 1u << (item & 31);
+      if (!(atomicOr(a.fbits + (item >> 5), bit) & bit)) a.flist[atomicAdd(a.qcount + 11, 1)] = item;
+    }
+  }
 
   // ---- a piece of a split item: publish the partial result (unnormalised
   // O, reference maxima and row-sum partials); the group's last piece to
@@ -619,9 +717,15 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   // slows every work group on it.
   if (piece >= 0) {
     if constexpr (!SWA && QB == 3 && NW == 8) {
+      if (oscale != 1.f) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int j = 0; j < QB; ++j) o[b][j] *= oscale;
+        oscale = 1.f;
+      }
       constexpr int SLOT = 384 * D + 2 * QB * NT;   // floats per slot (fwd_slot_floats)
       constexpr int ML = DB * QB * NT * 4;           // float offset of the maxima and row sums
-      __shared__ int last_piece;
       {
         float *slot = a.pslot + (size_t)piece * SLOT;
 #pragma unroll
@@ -687,7 +791,7 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     const float lsum = swap_sum(l[j]);
-    const float inv = 1.f / lsum;
+    const float inv = oscale / lsum;
     const int row = qbase + off_l[qloc0 + 16 * j + l16];
     if constexpr (PARTIAL) {
       const int ql = qloc0 + 16 * j + l16;
@@ -708,7 +812,12 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
       }
     }
   }
-  finish();
+  if constexpr (FIXUP) {
+    __syncthreads();
+    goto next_item;
+  } else {
+    finish();
+  }
 }
 
 
@@ -716,9 +825,9 @@ __global__ void zero_kernel(int32_t *p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
-template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL, bool SWA = false, bool SEP = false>
-hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
-  auto kern = sta_fwd_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, SEP>;
+template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL, bool SWA, bool SEP, bool FIXUP>
+hipError_t launch_kernel(const FwdArgs &a, int blocks, hipStream_t s) {
+  auto kern = sta_fwd_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, SEP, FIXUP>;
   const size_t lds = (size_t)fwd_lds_bytes(D, a.V, a.max_nkv) +
                      (PARTIAL || SEP ? (size_t)fwd_lds_step_bytes(a.V, a.max_nkv) : 0);
   if (lds > kMaxLds) return hipErrorInvalidValue;
@@ -727,8 +836,19 @@ hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3(a.n_blocks), dim3(NW * 64), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(NW * 64), lds, s, a);
   return hipGetLastError();
+}
+
+// The forward launch, then the fix-up launch (256 work groups, which exit
+// at once unless the forward marked work items whose V exceeds fp16's
+// range; those are redone with V scaled).  The fix-up kernel addresses K
+// and V through the tile tables (SEP off): it is the rare path.
+template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL, bool SWA = false, bool SEP = false>
+hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
+  hipError_t e = launch_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, SEP, false>(a, a.n_blocks, s);
+  if (e != hipSuccess) return e;
+  return launch_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, false, true>(a, 256, s);
 }
 
 template <int D, int QB, int NW, bool P, bool SEP = false>

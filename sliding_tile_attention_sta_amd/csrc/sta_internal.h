@@ -78,22 +78,32 @@ struct DeviceTables {
   void *block = nullptr;           // the single allocation holding all of the above
 };
 
-// Scratch of a forward launch of a plan with dynamic queues (the 384-query
-// kernel): 16 int32 queue words (the next free entry of each of the 9
-// queues, then the count of finished work groups and an "every queue is
-// empty" flag; the last work group to finish zeroes them), one int32 arrival
-// counter per split item (the last piece to arrive zeroes it), padded to
-// 256 B, then one partial-result slot per piece.  A slot holds the piece's
-// unnormalised O (QPI x D fp32, in the accumulator layout of the kernel's
-// threads) followed by each thread's reference maxima and row-sum partials
-// (2 x QB x threads fp32).
+// Scratch of a forward launch: 16 int32 queue words (the next free entry
+// of each of the 9 dynamic queues, the count of finished work groups, an
+// "every queue is empty" flag, the count of work items marked for the
+// fix-up kernel and the fix-up kernel's finished work groups), one int32
+// arrival counter per split item, one bit per work item code (marked:
+// redo with V scaled), all zero between launches (the last work group to
+// finish, the last piece to arrive and the fix-up kernel reset them); then
+// the list of marked items (one int32 per item code), padded to 256 B; then
+// one partial-result slot per piece.  A slot holds the piece's unnormalised
+// O (QPI x D fp32, in the accumulator layout of the kernel's threads)
+// followed by each thread's reference maxima and row-sum partials (2 x QB x
+// threads fp32).
 constexpr int kQueueWords = 16;
 constexpr long long fwd_slot_floats(int head_dim) {
   return 384LL * head_dim + 2LL * 3 * 512;
 }
-inline long long fwd_counter_bytes(long long groups) { return (4 * (kQueueWords + groups) + 255) / 256 * 256; }
-inline long long fwd_scratch_bytes(int head_dim, long long groups, long long pieces) {
-  return fwd_counter_bytes(groups) + 4LL * fwd_slot_floats(head_dim) * pieces;
+inline long long fwd_bit_words(long long items) { return (items + 31) / 32; }
+// int32 words that must be zero before a launch
+inline long long fwd_zero_words(long long groups, long long items) {
+  return kQueueWords + groups + fwd_bit_words(items);
+}
+inline long long fwd_counter_bytes(long long groups, long long items) {
+  return (4 * (fwd_zero_words(groups, items) + items) + 255) / 256 * 256;
+}
+inline long long fwd_scratch_bytes(int head_dim, long long groups, long long pieces, long long items) {
+  return fwd_counter_bytes(groups, items) + 4LL * fwd_slot_floats(head_dim) * pieces;
 }
 
 }  // namespace sta
@@ -141,6 +151,8 @@ struct sta_plan {
   int32_t variant = 0;
   int32_t qpi = 0;        // queries per work item
   int32_t subs = 0;       // work items per (b, head, query tile)
+  int64_t items() const { return (int64_t)batch * heads * n_tiles * subs; }   // forward item codes
+  long long fwd_scratch() const;                                              // bytes of forward scratch
 
   // Backward: inverse lists (query tiles whose window holds a key tile) and
   // the schedules of the dQ kernel (items of 32 * bwd_q_waves queries) and
@@ -189,3 +201,7 @@ sta_status build_swa_plan(int batch, int heads, int T, int H, int W, const int t
 void release_device_tables(sta_plan *plan);
 
 }  // namespace sta
+
+inline long long sta_plan::fwd_scratch() const {
+  return sta::fwd_scratch_bytes(D, n_groups, n_pieces, items());
+}

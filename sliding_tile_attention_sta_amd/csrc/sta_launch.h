@@ -33,7 +33,12 @@ struct FwdArgs {
   // and the launch's queue words (scratch; zero between launches).
   const int32_t *queue;
   int32_t qoff[10];
-  int32_t *qcount;
+  int32_t *qcount;         // scratch queue words (also the fix-up count and done counter)
+  // Work items whose O came out non-finite (V beyond fp16's range): a bit
+  // per item code and the list of marked items (scratch; zero between
+  // launches).
+  unsigned *fbits;
+  int32_t *flist;
   // Work items split by key range (entries -2 - p): per piece (item, first
   // step, end step, group), per group (first piece, pieces), and the
   // launch's scratch: an arrival counter per group (zero between launches)

@@ -498,7 +498,7 @@ sta_status sta_plan_get_info(const sta_plan *p, sta_plan_info *info) {
   info->partial_tiles = p->partial ? 1 : 0;
   info->split_items = p->n_groups;
   info->pieces = p->n_pieces;
-  info->scratch_bytes = p->dyn_blocks ? sta::fwd_scratch_bytes(p->D, p->n_groups, p->n_pieces) : 0;
+  info->scratch_bytes = p->fwd_scratch();
   info->launch_blocks = p->dyn_blocks ? p->dyn_blocks : (int64_t)p->sched.size();
   return STA_OK;
 }

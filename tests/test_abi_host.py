@@ -141,11 +141,14 @@ def test_schedule_covers_every_item_once_and_balances_xcds(name):
     if steps:
         split_cost = max(cost[(it // subs // info.n_tiles) % w.heads] for it in steps)
         assert all(cost[(c // subs // info.n_tiles) % w.heads] >= split_cost for c in whole[whole >= 0].tolist())
-    # the launch has more work groups than entries (dynamic queues) or exactly sched
+    # the launch has more work groups than entries (dynamic queues) or exactly
+    # sched; every forward has scratch (at least the fix-up marks of its items)
+    n_items = info.batch * info.heads * info.n_tiles * subs
+    assert info.scratch_bytes >= 4 * (16 + (n_items + 31) // 32 + n_items)
     if info.kernel_variant == 1:
-        assert info.launch_blocks >= len(s) and info.scratch_bytes > 0
+        assert info.launch_blocks >= len(s)
     else:
-        assert info.launch_blocks == len(s) and info.scratch_bytes == 0
+        assert info.launch_blocks == len(s)
 
 
 def test_tail_is_split_only_where_it_pays():

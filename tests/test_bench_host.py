@@ -41,7 +41,8 @@ def test_traffic_is_null_for_another_source_flags_or_workload(tmp_path):
         assert bench._measured_traffic(str(p), "sta_forward.hip", "720p", "bytes_per_launch") is None, name
     import hashlib
     src = os.path.join(ROOT, "sliding_tile_attention_sta_amd", "csrc", "sta_forward.hip")
-    t = dict(t, kernel_source_sha256=hashlib.sha256(open(src, "rb").read()).hexdigest())
+    t = dict(t, kernel_source_sha256=hashlib.sha256(open(src, "rb").read()).hexdigest(),
+             kernel_build_flags=bench._build_flags("sta_forward.hip"))
     p = tmp_path / "same.json"
     p.write_text(json.dumps(t))
     assert bench._measured_traffic(str(p), "sta_forward.hip", "720p", "bytes_per_launch") == t["bytes_per_launch"]
