@@ -114,11 +114,7 @@ def cpu_baseline(w, q, k, v, budget_s=12.0):
     import numpy as np
     from oracle import sta_oracle as O
     from sliding_tile_attention_sta_amd.synthetic import sample_query_tiles
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = _threads()
     grid = O.tile_grid(w.video, w.tile)
     V = w.tile[0] * w.tile[1] * w.tile[2]
     done_tiles, flops, t_used = 0, 0.0, 0.0
@@ -148,12 +144,23 @@ def cpu_baseline(w, q, k, v, budget_s=12.0):
     }
 
 
-def _threads():
+def _affinity():
     try:
-        from threadpoolctl import threadpool_info
-        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
-    except Exception:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
         return os.cpu_count() or 1
+
+
+def _threads():
+    """Host threads the oracle's numpy products can use: the BLAS thread
+    pool, bounded by the CPUs this process may run on."""
+    try:
+        import numpy  # noqa: F401  (loads the BLAS whose pool is read)
+        from threadpoolctl import threadpool_info
+        blas = int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        blas = _affinity()
+    return min(blas, _affinity())
 
 
 def _timed_tiles(w, heads_tiles, fn, flops_per_tile, budget_s):
@@ -240,14 +247,24 @@ def cpu_baseline_swa(w, q, k, v, toks, budget_s=10.0):
 
 
 def _cpu_model():
+    """Model name, family / model / stepping and the CPUs this process may
+    use, from /proc/cpuinfo and the scheduler's affinity mask."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if fields:
+                        break      # the first processor's block is enough
+                    continue
+                key, val = (x.strip() for x in line.split(":", 1))
+                fields.setdefault(key, val)
     except OSError:
         pass
-    return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    return f"{name} ({ids}; {_affinity()} CPUs in this process's affinity mask)" if ids else \
+        f"{name} ({_affinity()} CPUs in this process's affinity mask)"
 
 
 def _build_flags(source):

@@ -34,6 +34,9 @@
  *   - A plan is immutable after creation; it may be used from several host
  *     threads and streams at once.  Its device tables are uploaded once per
  *     device, on the first call that needs them.
+ *   - Test hook: with STA_TEST_FAIL_ALLOC=1 in the environment (read at
+ *     every allocation), every plan, device-table and scratch allocation of
+ *     the library fails and the call returns STA_ERR_ALLOC, leaking nothing.
  */
 #ifndef STA_H
 #define STA_H
@@ -89,7 +92,12 @@ typedef struct {
   int64_t launch_blocks;    /* work groups of one forward launch */
 } sta_plan_info;
 
-/* Build the host plan: tile grid, clamped per-head windows, per-(head, query
+/* Source: "Fast Video Generation with Sliding Tile Attention", index page,
+ * Abstract (non-overlapping 3D tiles, a window of whole tiles per query
+ * tile, window size set per head); gptget summary page, Methodology (the
+ * window slides tile by tile, so every (query tile, key tile) block is
+ * either fully attended or skipped).
+ * Build the host plan: tile grid, clamped per-head windows, per-(head, query
  * tile) key-tile lists (raster order of tile coordinates) and the launch
  * schedule (work items ordered by decreasing cost, spread evenly over the
  * chip's XCDs).  Host work only; no device is touched.
@@ -154,6 +162,19 @@ sta_status sta_plan_perm(const sta_plan *plan, int32_t *perm, int64_t cap);
 sta_status sta_plan_kv_tiles(const sta_plan *plan, int head, int q_tile, int32_t *out, int cap,
                              int *count);
 
+/* The same lists in the order the kernels walk them.  which = 0: the key
+ * tiles of query tile `tile` as the forward (and the backward's dQ kernel)
+ * visit them: raster order of (a mod wT, b mod wH, c mod wW) over the
+ * tile's window, a one-to-one map on any w consecutive tiles per axis, so
+ * query tiles whose windows overlap reach their shared key tiles at the
+ * same step.  which = 1: the query tiles whose window holds key tile
+ * `tile`, as the dK/dV kernel visits them: by the same residue of the query
+ * tile's coordinates, ties in raster order.  Buffer and error conventions
+ * as sta_plan_kv_tiles; STA_ERR_ARG also for token-wise SWA plans (no
+ * lists). */
+sta_status sta_plan_walk(const sta_plan *plan, int which, int head, int tile, int32_t *out, int cap,
+                         int *count);
+
 /* Query tiles (raster indices, ascending) whose window holds key tile
  * kv_tile for head head: the inverse of sta_plan_kv_tiles, walked by the
  * backward's dK/dV kernel.  Buffer and error conventions as sta_plan_kv_tiles. */
@@ -193,7 +214,13 @@ sta_status sta_plan_pieces(const sta_plan *plan, int32_t *out, int64_t cap, int6
 sta_status sta_plan_schedule_bwd(const sta_plan *plan, int which, int32_t *out, int64_t cap,
                                  int64_t *count);
 
-/* Gather a [batch, heads, N, head_dim] tensor from natural into tile-major
+/* Source: "Fast Video Generation with Sliding Tile Attention", gptget
+ * summary page, Technical Contribution (a tile-based design aligned with the
+ * hardware, which minimizes irregular memory access).  Reading used: the
+ * tokens of each tile are made contiguous in memory (tile-major order), so
+ * that every (query tile, key tile) pair is one dense block; the inverse
+ * permutation restores the video's raster order.
+ * Gather a [batch, heads, N, head_dim] tensor from natural into tile-major
  * token order (out[.., p, :] = in[.., perm[p], :]), or back.  dtype is the
  * element type of both tensors.  Bound by HBM bandwidth. */
 sta_status sta_tile_reorder(const sta_plan *plan, const void *in, void *out, sta_dtype dtype,
@@ -201,15 +228,22 @@ sta_status sta_tile_reorder(const sta_plan *plan, const void *in, void *out, sta
 sta_status sta_tile_unreorder(const sta_plan *plan, const void *in, void *out, sta_dtype dtype,
                               void *stream);
 
-/* STA forward with a plan.  q, k, v: [batch, heads, N, head_dim] of in_dtype;
+/* Source: "Fast Video Generation with Sliding Tile Attention", index page,
+ * Abstract, and gptget summary page, Methodology: inside its window a query
+ * tile takes ordinary softmax attention over every key of the window's
+ * tiles (the formula at the top of this file); no block is partly masked.
+ * STA forward with a plan.  q, k, v: [batch, heads, N, head_dim] of in_dtype;
  * out: same shape, out_dtype (STA_F32 or STA_BF16).  All four tensors use the
  * token order given by layout.  scale > 0 multiplies Q.K (usually
  * 1/sqrt(head_dim)).
  * Precision: Q.K^T runs on bf16 MFMA (STA_F32 q and k are rounded to bf16,
  * nearest-even, as they are loaded); the softmax runs in fp32; P.V runs on
  * fp16 MFMA with P rounded to fp16 and V converted to fp16 (exact for bf16
- * values, nearest-even for fp32), all accumulated in fp32.  V must lie
- * within the fp16 range, |v| <= 65504: larger entries become infinities.
+ * values, nearest-even for fp32), all accumulated in fp32.  V beyond the
+ * fp16 range (|v| > 65504, possible in bf16 and fp32): a work item whose
+ * output comes out non-finite is redone by a second kernel of the same
+ * call with V multiplied by 2^-e and O by 2^e (e from the largest |v| of
+ * the item's keys), so any finite V gives a finite, correctly scaled O.
  * Inputs must be finite.  The result does not depend on the order in which
  * key tiles are visited beyond fp32 rounding. */
 sta_status sta_forward_plan(const sta_plan *plan, const void *q, const void *k, const void *v,
@@ -280,7 +314,8 @@ sta_status sta_backward_plan(const sta_plan *plan, const void *q, const void *k,
 
 /* Same, building (or finding in a process-wide cache keyed by every shape
  * and window argument) the plan itself.  Cached plans live until
- * sta_clear_plan_cache or process exit. */
+ * sta_clear_plan_cache or process exit.  Thread-safe: several threads may
+ * call it at once, also while another clears the cache. */
 sta_status sta_forward(const void *q, const void *k, const void *v, void *out, int batch, int heads,
                        int T, int H, int W, const int tile[3], const int *window, int head_dim,
                        float scale, sta_dtype in_dtype, sta_dtype out_dtype, sta_layout layout,
@@ -318,6 +353,23 @@ sta_status sta_window_errors(const void *q, const void *k, const void *v, int ba
 sta_status sta_window_select(int heads, const int grid[3], const int *candidates, int n_cand,
                              const double *err, double threshold, int *window_out);
 
+/* The whole search over n_samples calibration inputs: q[s], k[s], v[s]
+ * (arrays of n_samples DEVICE pointers, each tensor as in
+ * sta_window_errors).  For every sample, the errors of sta_window_errors;
+ * their arithmetic mean over the samples, summed in sample order (the
+ * pages' per-head configuration reads several prompts; reading: errors
+ * averaged before the choice); window_out[3h .. 3h+2] = the window that
+ * sta_window_select chooses from the mean under threshold.  err_out: HOST
+ * buffer of heads * n_cand doubles for the mean errors, or NULL.  The call
+ * synchronises stream.
+ * Errors: as sta_window_errors; STA_ERR_ARG for n_samples < 1 or a NULL
+ * pointer in the arrays. */
+sta_status sta_window_search(const void *const *q, const void *const *k, const void *const *v,
+                             int n_samples, int batch, int heads, int T, int H, int W, const int tile[3],
+                             int head_dim, float scale, sta_dtype in_dtype, sta_layout layout,
+                             const int *candidates, int n_cand, double threshold, double *err_out,
+                             int *window_out, void *stream);
+
 /* Host only.  The default candidate set for a grid: on each axis every odd
  * extent below the axis length, and the axis length itself; all
  * combinations in raster order, written as triples to out (cap triples).
@@ -325,7 +377,8 @@ sta_status sta_window_select(int heads, const int grid[3], const int *candidates
  * STA_ERR_ARG). */
 sta_status sta_window_candidates(const int grid[3], int *out, int cap, int *count);
 
-/* Destroy every cached plan.  Not safe while another thread is in sta_forward. */
+/* Drop every cached plan.  Safe while other threads are in sta_forward: a
+ * plan that a call is still using is destroyed when that call returns. */
 sta_status sta_clear_plan_cache(void);
 
 /* Static, human-readable name of a status code. */

@@ -40,7 +40,7 @@ import numpy as np
 
 from . import sta_oracle as F
 
-__all__ = ["window_cost", "window_errors", "select_windows", "odd_candidates"]
+__all__ = ["window_cost", "window_errors", "select_windows", "odd_candidates", "search"]
 
 
 def window_cost(window: Sequence[int], grid: Sequence[int]) -> int:
@@ -92,3 +92,19 @@ def select_windows(err: np.ndarray, candidates, grid: Sequence[int], threshold: 
                 best = (key, tuple(int(x) for x in w))
         out.append(best[1] if best is not None else tuple(int(n) for n in grid))
     return out
+
+
+def search(samples, video: Sequence[int], tile: Sequence[int], candidates, threshold: float,
+           scale: float | None = None):
+    """Readings W1-W4 over several calibration inputs: each sample's
+    per-(head, candidate) errors (W1, W2), their arithmetic mean over the
+    samples (W4), and the choice from the mean (W3).  samples: sequence of
+    (q, k, v), each [B, heads, N, D].  Returns (windows, mean errors)."""
+    errs = [window_errors(q, k, v, video, tile, candidates, scale=scale) for q, k, v in samples]
+    if not errs:
+        raise ValueError("no calibration samples")
+    mean = np.zeros_like(errs[0])
+    for e in errs:
+        mean += e
+    mean /= len(errs)
+    return select_windows(mean, candidates, F.tile_grid(video, tile), threshold), mean

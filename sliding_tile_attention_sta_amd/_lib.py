@@ -52,6 +52,7 @@ SIGNATURES = {
     "sta_plan_schedule": (_I, [_P, _I32P, _I64, ctypes.POINTER(_I64)]),
     "sta_plan_pieces": (_I, [_P, _I32P, _I64, ctypes.POINTER(_I64)]),
     "sta_plan_q_tiles": (_I, [_P, _I, _I, _I32P, _I, _IP]),
+    "sta_plan_walk": (_I, [_P, _I, _I, _I, _I32P, _I, _IP]),
     "sta_plan_schedule_bwd": (_I, [_P, _I, _I32P, _I64, ctypes.POINTER(_I64)]),
     "sta_tile_reorder": (_I, [_P, _P, _P, _I, _P]),
     "sta_tile_unreorder": (_I, [_P, _P, _P, _I, _P]),
@@ -64,6 +65,9 @@ SIGNATURES = {
                          _I, _I, _I, _P]),
     "sta_window_errors": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _IP, _I, ctypes.c_float, _I, _I, _IP, _I,
                                ctypes.POINTER(ctypes.c_double), _P]),
+    "sta_window_search": (_I, [ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P), _I, _I, _I, _I, _I,
+                               _I, _IP, _I, ctypes.c_float, _I, _I, _IP, _I, ctypes.c_double,
+                               ctypes.POINTER(ctypes.c_double), _IP, _P]),
     "sta_window_select": (_I, [_I, _IP, _IP, _I, ctypes.POINTER(ctypes.c_double), ctypes.c_double, _IP]),
     "sta_window_candidates": (_I, [_IP, _IP, _I, _IP]),
     "sta_clear_plan_cache": (_I, []),

@@ -126,6 +126,16 @@ class Plan:
                 "sta_plan_kv_tiles")
         return list(buf[:cnt.value])
 
+    def walk(self, which: int, head: int, tile: int) -> list[int]:
+        """The lists in kernel walk order: which=0, the key tiles of query
+        tile ``tile``; which=1, the query tiles that see key tile ``tile``."""
+        cnt = ctypes.c_int()
+        L.lib().sta_plan_walk(self._h, which, head, tile, None, 0, ctypes.byref(cnt))
+        buf = (ctypes.c_int32 * max(1, cnt.value))()
+        L.check(L.lib().sta_plan_walk(self._h, which, head, tile, buf, cnt.value, ctypes.byref(cnt)),
+                "sta_plan_walk")
+        return list(buf[:cnt.value])
+
     def q_tiles(self, head: int, kv_tile: int) -> list[int]:
         cnt = ctypes.c_int()
         L.lib().sta_plan_q_tiles(self._h, head, kv_tile, None, 0, ctypes.byref(cnt))
@@ -395,23 +405,39 @@ def window_select(err, candidates, grid, threshold: float) -> list[tuple[int, in
 
 def window_search(samples, tile, threshold: float, candidates=None, scale: float | None = None,
                   layout: str = "natural", stream=None):
-    """Per-head windows from calibration inputs: ``samples`` is an iterable
-    of (q, k, v) in natural [B, heads, T, H, W, D] order.  The errors are
-    averaged over the samples before the choice.  Returns (windows, mean
-    errors, candidates)."""
-    errs, video = [], None
-    for q, k, v in samples:
-        if video is not None and tuple(q.shape[2:5]) != video:
-            raise ValueError("calibration samples must share one video shape")
-        video = tuple(q.shape[2:5])
-        grid = tuple(e // t for e, t in zip(video, tile))
-        cands = candidates if candidates is not None else window_candidates(grid)
-        errs.append(window_errors(q, k, v, tile, cands, scale=scale, layout=layout, stream=stream))
-    if not errs:
+    """Per-head windows from calibration inputs (``sta_window_search``):
+    ``samples`` is a sequence of (q, k, v) in natural [B, heads, T, H, W, D]
+    order, all of one shape and dtype.  The library averages the errors over
+    the samples before the choice.  Returns (windows, mean errors,
+    candidates)."""
+    import numpy as np
+    samples = [tuple(s) for s in samples]
+    if not samples:
         raise ValueError("no calibration samples")
-    mean = sum(errs) / len(errs)
-    grid = tuple(e // t for e, t in zip(video, tile))
-    return window_select(mean, cands, grid, threshold), mean, cands
+    shapes = {tuple(x.shape) for s in samples for x in s}
+    dtypes = {x.dtype for s in samples for x in s}
+    if len(shapes) != 1 or len(dtypes) != 1:
+        raise ValueError("calibration samples must share one shape and dtype")
+    for s in samples:
+        _video_inputs(*s, None)
+    q0, k0, v0 = samples[0]
+    B, heads, T, H, W, D = _video_inputs(q0, k0, v0, None)
+    grid = tuple(e // t for e, t in zip((T, H, W), tile))
+    cands = [tuple(int(x) for x in w) for w in (candidates if candidates is not None else window_candidates(grid))]
+    n = len(cands)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    arr = [(ctypes.c_void_p * len(samples))(*(_ptr(s[i]) for s in samples)) for i in range(3)]
+    err = (ctypes.c_double * (heads * n))()
+    out = (ctypes.c_int * (3 * heads))()
+    with _scope([x for s in samples for x in s], stream):
+        st = L.lib().sta_window_search(*arr, len(samples), int(B), int(heads), int(T), int(H), int(W),
+                                       _ints(tile), int(D), float(scale), _DTYPES[q0.dtype], _LAYOUTS[layout],
+                                       _ints([x for w in cands for x in w]), n, float(threshold), err, out,
+                                       _stream(stream))
+        L.check(st, "sta_window_search")
+    windows = [tuple(out[3 * h:3 * h + 3]) for h in range(heads)]
+    return windows, np.array(err[:], dtype=np.float64).reshape(heads, n), cands
 
 
 def sta_clear_plan_cache() -> None:

@@ -20,21 +20,29 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Upload the plan's tables to the current device once; later calls reuse them.
-sta_status device_tables(const sta_plan *p, DeviceTables *out) {
+// Orders `stream` after the upload of the tables in t (a no-op on the
+// stream that uploaded them).
+sta_status wait_upload(const DeviceTables &t, void *stream) {
+  if (t.ready == nullptr || t.upload_stream == stream) return STA_OK;
+  return hipStreamWaitEvent(static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(t.ready), 0) == hipSuccess
+             ? STA_OK
+             : STA_ERR_HIP;
+}
+
+// Upload the plan's tables to the current device once, with asynchronous
+// copies on the caller's stream (the host sources live as long as the plan);
+// later calls reuse them.
+sta_status device_tables(const sta_plan *p, void *stream, DeviceTables *out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return STA_ERR_HIP;
   std::lock_guard<std::mutex> lock(p->mu);
   auto it = p->dev.find(dev);
   if (it != p->dev.end()) {
     *out = it->second;
-    return STA_OK;
+    return wait_upload(it->second, stream);
   }
-  std::vector<int32_t> base_tm(p->n_tiles), off_tm(p->V);
-  for (int i = 0; i < p->n_tiles; ++i) base_tm[i] = i * p->V;
-  for (int j = 0; j < p->V; ++j) off_tm[j] = j;
   const std::vector<int32_t> *parts[] = {&p->kv_off, &p->kv_idx,   &p->sched,    &p->base_nat,
-                                         &p->off_nat, &base_tm,     &off_tm,      &p->q_off,
+                                         &p->off_nat, &p->base_tm,  &p->off_tm,   &p->q_off,
                                          &p->q_idx,   &p->sched_dq, &p->sched_dkdv, &p->kmask,
                                          &p->swin,    &p->ptab,     &p->gtab,     &p->queue};
   constexpr int kParts = sizeof(parts) / sizeof(parts[0]);
@@ -44,15 +52,26 @@ sta_status device_tables(const sta_plan *p, DeviceTables *out) {
     total += (parts[i]->size() * sizeof(int32_t) + 255) & ~size_t(255);
   }
   void *block = nullptr;
-  if (hipMalloc(&block, total) != hipSuccess) return STA_ERR_ALLOC;
+  if (test_fail_alloc() || hipMalloc(&block, total) != hipSuccess) return STA_ERR_ALLOC;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t ready = nullptr;
+  auto fail = [&](sta_status e) {
+    (void)hipStreamSynchronize(s);
+    if (ready) (void)hipEventDestroy(ready);
+    (void)hipFree(block);
+    return e;
+  };
   for (int i = 0; i < kParts; ++i) {
     if (parts[i]->empty()) continue;
-    if (hipMemcpy(static_cast<char *>(block) + offs[i], parts[i]->data(),
-                  parts[i]->size() * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess) {
-      (void)hipFree(block);
-      return STA_ERR_HIP;
-    }
+    if (hipMemcpyAsync(static_cast<char *>(block) + offs[i], parts[i]->data(),
+                       parts[i]->size() * sizeof(int32_t), hipMemcpyHostToDevice, s) != hipSuccess)
+      return fail(STA_ERR_HIP);
   }
+  if (hipEventCreateWithFlags(&ready, hipEventDisableTiming) != hipSuccess) {
+    ready = nullptr;
+    return fail(STA_ERR_HIP);
+  }
+  if (hipEventRecord(ready, s) != hipSuccess) return fail(STA_ERR_HIP);
   DeviceTables t;
   char *b = static_cast<char *>(block);
   t.kv_off = reinterpret_cast<int32_t *>(b + offs[0]);
@@ -72,21 +91,27 @@ sta_status device_tables(const sta_plan *p, DeviceTables *out) {
   t.gtab = p->gtab.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[14]);
   t.queue = p->queue.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[15]);
   t.block = block;
-  p->dev[dev] = t;
+  t.upload_stream = stream;
+  t.ready = ready;
+  try {
+    p->dev[dev] = t;
+  } catch (const std::bad_alloc &) {
+    return fail(STA_ERR_ALLOC);
+  }
   *out = t;
   return STA_OK;
 }
 
 // The plan's tables on the current device if they were uploaded before
 // (no allocation); STA_ERR_UNSUPPORTED if not.
-sta_status existing_device_tables(const sta_plan *p, DeviceTables *out) {
+sta_status existing_device_tables(const sta_plan *p, void *stream, DeviceTables *out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return STA_ERR_HIP;
   std::lock_guard<std::mutex> lock(p->mu);
   auto it = p->dev.find(dev);
   if (it == p->dev.end()) return STA_ERR_UNSUPPORTED;
   *out = it->second;
-  return STA_OK;
+  return wait_upload(it->second, stream);
 }
 
 // Scratch of sta_forward_plan_noalloc: a fixed array in device memory that
@@ -132,7 +157,7 @@ sta_status forward_scratch(const sta_plan *p, void *stream, void **out) {
     return STA_OK;
   }
   void *buf = nullptr;
-  if (hipMalloc(&buf, (size_t)p->fwd_scratch()) != hipSuccess)
+  if (test_fail_alloc() || hipMalloc(&buf, (size_t)p->fwd_scratch()) != hipSuccess)
     return STA_ERR_ALLOC;
   if (launch_zero(static_cast<int32_t *>(buf), (int)fwd_zero_words(p->n_groups, p->items()),
                   static_cast<hipStream_t>(stream)) != hipSuccess) {
@@ -159,7 +184,7 @@ sta_status reorder(const sta_plan *p, const void *in, void *out, sta_dtype dtype
   if (overlaps(in, bytes, out, bytes)) return STA_ERR_ARG;
   if (p->partial || p->swa) return STA_ERR_UNSUPPORTED;   // tile-major order needs whole tiles
   DeviceTables t;
-  sta_status st = device_tables(p, &t);
+  sta_status st = device_tables(p, stream, &t);
   if (st != STA_OK) return st;
   ReorderArgs a;
   a.in = in;
@@ -174,13 +199,6 @@ sta_status reorder(const sta_plan *p, const void *in, void *out, sta_dtype dtype
   return launch_reorder(a, static_cast<hipStream_t>(stream)) == hipSuccess ? STA_OK : STA_ERR_HIP;
 }
 
-struct CacheKey {
-  std::vector<int> v;
-  bool operator<(const CacheKey &o) const { return v < o.v; }
-};
-std::mutex g_cache_mu;
-std::map<CacheKey, sta_plan *> g_cache;
-
 }  // namespace
 
 void release_device_tables(sta_plan *p) {
@@ -189,16 +207,21 @@ void release_device_tables(sta_plan *p) {
   int cur = -1;
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
   // Work launched with the plan may still read its tables and scratch: each
-  // device finishes its queued work before its buffers are freed.
-  std::map<int, bool> synced;
+  // device finishes its queued work before its buffers are freed.  (No
+  // allocation here: destroying a plan cannot fail.)
+  bool synced[kMaxDevices] = {};
   auto sync = [&](int dev) {
-    if (synced[dev]) return true;
+    if (dev >= 0 && dev < kMaxDevices && synced[dev]) return true;
     if (hipSetDevice(dev) != hipSuccess) return false;
     (void)hipDeviceSynchronize();
-    return synced[dev] = true;
+    if (dev >= 0 && dev < kMaxDevices) synced[dev] = true;
+    return true;
   };
   for (auto &kv : p->dev)
-    if (sync(kv.first)) (void)hipFree(kv.second.block);
+    if (sync(kv.first)) {
+      if (kv.second.ready) (void)hipEventDestroy(static_cast<hipEvent_t>(kv.second.ready));
+      (void)hipFree(kv.second.block);
+    }
   for (auto &kv : p->scratch)
     if (sync(kv.first.first)) (void)hipFree(kv.second);
   if (have_cur) (void)hipSetDevice(cur);
@@ -250,7 +273,7 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   void *scratch = nullptr;
   if (no_alloc) {
     if (p->fwd_scratch() > (long long)kStaticScratchBytes) return STA_ERR_UNSUPPORTED;
-    sta_status st = existing_device_tables(p, &t);
+    sta_status st = existing_device_tables(p, stream, &t);
     if (st != STA_OK) return st;
     st = static_scratch(&scratch);
     if (st != STA_OK) return st;
@@ -258,7 +281,7 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
                     static_cast<hipStream_t>(stream)) != hipSuccess)
       return STA_ERR_HIP;
   } else {
-    sta_status st = sta::device_tables(p, &t);
+    sta_status st = sta::device_tables(p, stream, &t);
     if (st != STA_OK) return st;
     st = forward_scratch(p, stream, &scratch);
     if (st != STA_OK) return st;
@@ -332,7 +355,7 @@ sta_status backward(const sta_plan *p, const void *q, const void *k, const void 
       if (overlaps(written[i], wbytes[i], written[j], wbytes[j])) return STA_ERR_ARG;
   }
   DeviceTables t;
-  sta_status st = device_tables(p, &t);
+  sta_status st = device_tables(p, stream, &t);
   if (st != STA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_bwd_delta(out, dout, delta, (int64_t)rows, p->D, out_dtype == STA_F32, in_dtype == STA_F32,
@@ -406,35 +429,10 @@ sta_status sta_forward(const void *q, const void *k, const void *v, void *out, i
                        int T, int H, int W, const int tile[3], const int *window, int head_dim,
                        float scale, sta_dtype in_dtype, sta_dtype out_dtype, sta_layout layout,
                        void *stream) {
-  if (!tile || !window || heads < 1) return STA_ERR_ARG;
-  sta::CacheKey key;
-  key.v = {batch, heads, T, H, W, tile[0], tile[1], tile[2], head_dim};
-  key.v.insert(key.v.end(), window, window + 3 * heads);
-  sta_plan *p = nullptr;
-  {
-    std::lock_guard<std::mutex> lock(sta::g_cache_mu);
-    auto it = sta::g_cache.find(key);
-    if (it != sta::g_cache.end()) {
-      p = it->second;
-    } else {
-      sta_status st = sta::build_plan(batch, heads, T, H, W, tile, window, head_dim, false, &p);
-      if (st != STA_OK) return st;
-      try {
-        sta::g_cache[key] = p;
-      } catch (...) {
-        sta_plan_destroy(p);
-        return STA_ERR_ALLOC;
-      }
-    }
-  }
-  return sta_forward_plan(p, q, k, v, out, scale, in_dtype, out_dtype, layout, stream);
-}
-
-sta_status sta_clear_plan_cache(void) {
-  std::lock_guard<std::mutex> lock(sta::g_cache_mu);
-  for (auto &kv : sta::g_cache) sta_plan_destroy(kv.second);
-  sta::g_cache.clear();
-  return STA_OK;
+  sta_status st = STA_OK;
+  const std::shared_ptr<sta_plan> p = sta::cached_plan(batch, heads, T, H, W, tile, window, head_dim, &st);
+  if (!p) return st;
+  return sta_forward_plan(p.get(), q, k, v, out, scale, in_dtype, out_dtype, layout, stream);
 }
 
 }  // extern "C"

@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -76,6 +77,11 @@ struct DeviceTables {
   int32_t *ptab = nullptr;         // split items: 4 per piece (item, first step, end step, group)
   int32_t *gtab = nullptr;         // split items: 2 per group (first piece, piece count)
   void *block = nullptr;           // the single allocation holding all of the above
+  // The upload runs on the stream of the call that made it; `ready` (a
+  // hipEvent_t) is recorded after it, and a call on another stream waits
+  // for it before its first launch.
+  void *upload_stream = nullptr;
+  void *ready = nullptr;
 };
 
 // Scratch of a forward launch: 16 int32 queue words (the next free entry
@@ -146,6 +152,7 @@ struct sta_plan {
   int32_t qoff[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   int32_t dyn_blocks = 0;
   std::vector<int32_t> base_nat, off_nat;
+  std::vector<int32_t> base_tm, off_tm;   // tile-major layout: tile * V, identity
   int64_t pairs = 0;
   int32_t max_nkv = 0;    // longest key-tile list
   int32_t variant = 0;
@@ -199,6 +206,20 @@ sta_status build_swa_plan(int batch, int heads, int T, int H, int W, const int t
 
 // Releases device tables; defined in sta_api.hip (needs HIP).
 void release_device_tables(sta_plan *plan);
+
+// Process-wide cache of STA plans for sta_forward (host only; defined in
+// sta_plan.cpp).  Callers hold a shared reference, so that clearing the
+// cache never frees a plan that a call is still using: the last reference
+// destroys it.  Returns nullptr and sets *status when the plan cannot be
+// built.
+std::shared_ptr<sta_plan> cached_plan(int batch, int heads, int T, int H, int W, const int tile[3],
+                                      const int *window, int head_dim, sta_status *status);
+void clear_plan_cache();
+
+// Test hook: true when the environment holds STA_TEST_FAIL_ALLOC=1; every
+// plan, device-table and scratch allocation of the library then fails with
+// STA_ERR_ALLOC.
+bool test_fail_alloc();
 
 }  // namespace sta
 

@@ -8,7 +8,11 @@
 // centred on its query tile and shifted inward at the borders.
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
 #include <functional>
 #include <new>
 #include <numeric>
@@ -218,6 +222,7 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
   sta_plan *p = new (std::nothrow) sta_plan();
   if (!p) return STA_ERR_ALLOC;
   try {
+    if (test_fail_alloc()) throw std::bad_alloc();
     p->batch = batch; p->heads = heads; p->T = T; p->H = H; p->W = W; p->D = head_dim;
     for (int d = 0; d < 3; ++d) {
       p->tile[d] = tile[d];
@@ -284,6 +289,10 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
       const int lt = j / (tile[1] * tile[2]), ly = (j / tile[2]) % tile[1], lz = j % tile[2];
       p->off_nat[j] = (lt * H + ly) * W + lz;
     }
+    p->base_tm.resize(p->n_tiles);
+    for (int qt = 0; qt < p->n_tiles; ++qt) p->base_tm[qt] = qt * p->V;
+    p->off_tm.resize(p->V);
+    std::iota(p->off_tm.begin(), p->off_tm.end(), 0);
     p->sep_nat = true;
     for (int j = 0; j < p->V; ++j)
       if (p->off_nat[j] - p->off_nat[j / kKeyBlock * kKeyBlock] != p->off_nat[j % kKeyBlock] - p->off_nat[0])
@@ -382,6 +391,7 @@ sta_status build_swa_plan(int batch, int heads, int T, int H, int W, const int t
   sta_plan *p = new (std::nothrow) sta_plan();
   if (!p) return STA_ERR_ALLOC;
   try {
+    if (test_fail_alloc()) throw std::bad_alloc();
     p->batch = batch; p->heads = heads; p->T = T; p->H = H; p->W = W; p->D = head_dim;
     for (int d = 0; d < 3; ++d) { p->tile[d] = tile[d]; p->grid[d] = ext[d] / tile[d]; }
     p->V = (int32_t)V64;
@@ -428,6 +438,10 @@ sta_status build_swa_plan(int batch, int heads, int T, int H, int W, const int t
       const int lt = j / (tile[1] * tile[2]), ly = (j / tile[2]) % tile[1], lz = j % tile[2];
       p->off_nat[j] = (lt * H + ly) * W + lz;
     }
+    p->base_tm.resize(p->n_tiles);
+    for (int qt = 0; qt < p->n_tiles; ++qt) p->base_tm[qt] = qt * p->V;
+    p->off_tm.resize(p->V);
+    std::iota(p->off_tm.begin(), p->off_tm.end(), 0);
     if (p->variant == kTile384)
       build_forward_queues(p, cost_off, 1, 1, false);
     else
@@ -440,9 +454,69 @@ sta_status build_swa_plan(int batch, int heads, int T, int H, int W, const int t
   return STA_OK;
 }
 
+// The n entries at src in ascending order, the first cap of them written to
+// out (no allocation: the query entry points never throw).
+sta_status sorted_list(const int32_t *src, int32_t n, int32_t *out, int cap, int *count) {
+  *count = n;
+  if (!out && cap > 0) return STA_ERR_ARG;
+  if (cap > 0) std::partial_sort_copy(src, src + n, out, out + std::min(cap, n));
+  return n > cap ? STA_ERR_ARG : STA_OK;
+}
+
+bool test_fail_alloc() {
+  const char *e = std::getenv("STA_TEST_FAIL_ALLOC");
+  return e != nullptr && std::strcmp(e, "1") == 0;
+}
+
+namespace {
+std::mutex g_cache_mu;
+std::map<std::vector<int>, std::shared_ptr<sta_plan>> g_cache;
+}  // namespace
+
+std::shared_ptr<sta_plan> cached_plan(int batch, int heads, int T, int H, int W, const int tile[3],
+                                      const int *window, int head_dim, sta_status *status) {
+  *status = STA_OK;
+  if (!tile || !window || heads < 1) {
+    *status = STA_ERR_ARG;
+    return nullptr;
+  }
+  try {
+    std::vector<int> key = {batch, heads, T, H, W, tile[0], tile[1], tile[2], head_dim};
+    key.insert(key.end(), window, window + 3 * (size_t)heads);
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    auto it = g_cache.find(key);
+    if (it != g_cache.end()) return it->second;
+    sta_plan *p = nullptr;
+    *status = build_plan(batch, heads, T, H, W, tile, window, head_dim, false, &p);
+    if (*status != STA_OK) return nullptr;
+    // (if the shared state cannot be allocated, the constructor destroys p)
+    std::shared_ptr<sta_plan> sp(p, [](sta_plan *x) { sta_plan_destroy(x); });
+    g_cache.emplace(std::move(key), sp);
+    return sp;
+  } catch (const std::bad_alloc &) {
+    *status = STA_ERR_ALLOC;
+    return nullptr;
+  }
+}
+
+void clear_plan_cache() {
+  std::map<std::vector<int>, std::shared_ptr<sta_plan>> old;
+  {
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    old.swap(g_cache);
+  }
+  // the cache's references are dropped here, outside the lock; a plan still
+  // in use by a call is destroyed when that call releases it
+}
+
 }  // namespace sta
 
 extern "C" {
+
+sta_status sta_clear_plan_cache(void) {
+  sta::clear_plan_cache();
+  return STA_OK;
+}
 
 sta_status sta_swa_plan_create(int batch, int heads, int T, int H, int W, const int tile[3],
                                const int *window_tokens, int head_dim, sta_plan **out) {
@@ -516,12 +590,7 @@ sta_status sta_plan_kv_tiles(const sta_plan *p, int head, int q_tile, int32_t *o
   if (!p || !count || head < 0 || head >= p->heads || q_tile < 0 || q_tile >= p->n_tiles)
     return STA_ERR_ARG;
   const size_t i = (size_t)head * p->n_tiles + q_tile;
-  std::vector<int32_t> list(p->kv_idx.begin() + p->kv_off[i], p->kv_idx.begin() + p->kv_off[i + 1]);
-  std::sort(list.begin(), list.end());
-  *count = (int)list.size();
-  if (!out && cap > 0) return STA_ERR_ARG;
-  for (int j = 0; j < cap && j < (int)list.size(); ++j) out[j] = list[j];
-  return (int)list.size() > cap ? STA_ERR_ARG : STA_OK;
+  return sta::sorted_list(p->kv_idx.data() + p->kv_off[i], p->kv_off[i + 1] - p->kv_off[i], out, cap, count);
 }
 
 sta_status sta_plan_q_tiles(const sta_plan *p, int head, int kv_tile, int32_t *out, int cap,
@@ -529,12 +598,21 @@ sta_status sta_plan_q_tiles(const sta_plan *p, int head, int kv_tile, int32_t *o
   if (!p || !count || head < 0 || head >= p->heads || kv_tile < 0 || kv_tile >= p->n_tiles)
     return STA_ERR_ARG;
   const size_t i = (size_t)head * p->n_tiles + kv_tile;
-  std::vector<int32_t> list(p->q_idx.begin() + p->q_off[i], p->q_idx.begin() + p->q_off[i + 1]);
-  std::sort(list.begin(), list.end());
-  const int n = (int)list.size();
+  return sta::sorted_list(p->q_idx.data() + p->q_off[i], p->q_off[i + 1] - p->q_off[i], out, cap, count);
+}
+
+sta_status sta_plan_walk(const sta_plan *p, int which, int head, int tile, int32_t *out, int cap, int *count) {
+  if (!p || !count || (which != 0 && which != 1) || head < 0 || head >= p->heads || tile < 0 ||
+      tile >= p->n_tiles || p->swa)
+    return STA_ERR_ARG;
+  const std::vector<int32_t> &off = which == 0 ? p->kv_off : p->q_off;
+  const std::vector<int32_t> &idx = which == 0 ? p->kv_idx : p->q_idx;
+  if (off.empty()) return STA_ERR_ARG;
+  const size_t i = (size_t)head * p->n_tiles + tile;
+  const int n = off[i + 1] - off[i];
   *count = n;
   if (!out && cap > 0) return STA_ERR_ARG;
-  for (int j = 0; j < cap && j < n; ++j) out[j] = list[j];
+  for (int j = 0; j < cap && j < n; ++j) out[j] = idx[(size_t)off[i] + j];
   return n > cap ? STA_ERR_ARG : STA_OK;
 }
 
@@ -575,19 +653,20 @@ sta_status sta_window_candidates(const int grid[3], int *out, int cap, int *coun
   if (!grid || !count) return STA_ERR_ARG;
   for (int d = 0; d < 3; ++d)
     if (grid[d] < 1) return STA_ERR_ARG;
-  std::vector<int> axis[3];
-  for (int d = 0; d < 3; ++d) {
-    for (int w = 1; w < grid[d]; w += 2) axis[d].push_back(w);
-    axis[d].push_back(grid[d]);
-  }
-  const int n = (int)(axis[0].size() * axis[1].size() * axis[2].size());
-  *count = n;
+  // per axis: the odd extents below the axis length (grid / 2 of them),
+  // then the length itself
+  int na[3];
+  for (int d = 0; d < 3; ++d) na[d] = grid[d] / 2 + 1;
+  auto value = [&](int d, int j) { return j < grid[d] / 2 ? 2 * j + 1 : grid[d]; };
+  const long long n = (long long)na[0] * na[1] * na[2];
+  if (n > INT32_MAX) return STA_ERR_ARG;
+  *count = (int)n;
   if (cap < n || !out) return STA_ERR_ARG;
   int i = 0;
-  for (int a : axis[0])
-    for (int b : axis[1])
-      for (int c : axis[2]) {
-        out[3 * i] = a; out[3 * i + 1] = b; out[3 * i + 2] = c;
+  for (int a = 0; a < na[0]; ++a)
+    for (int b = 0; b < na[1]; ++b)
+      for (int c = 0; c < na[2]; ++c) {
+        out[3 * i] = value(0, a); out[3 * i + 1] = value(1, b); out[3 * i + 2] = value(2, c);
         ++i;
       }
   return STA_OK;

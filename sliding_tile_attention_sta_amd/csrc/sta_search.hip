@@ -18,6 +18,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <new>
 #include <vector>
 
 #include "sta_internal.h"
@@ -98,19 +99,30 @@ sta_status sta_window_errors(const void *q, const void *k, const void *v, int ba
   for (int d = 0; d < 3; ++d)
     if (ext[d] % tile[d] != 0) return STA_ERR_SHAPE;
   const int grid[3] = {T / tile[0], H / tile[1], W / tile[2]};
+  const int64_t plane = (int64_t)T * H * W * head_dim;
+  const size_t out_bytes = (size_t)batch * heads * plane * sizeof(float);
+  const size_t part_count = (size_t)batch * heads * sta::kRedBlocksPerPlane * 2;
+  // Host buffers first: nothing below allocates on the host once work is
+  // queued (the entry point never throws).
+  std::vector<int> win;
+  std::vector<double> host;
+  try {
+    win.resize((size_t)heads * 3);
+    host.resize(part_count);
+  } catch (const std::bad_alloc &) {
+    return STA_ERR_ALLOC;
+  }
 
   // Full-attention plan (window = grid for every head) and its output.
-  std::vector<int> win((size_t)heads * 3);
   for (int h = 0; h < heads; ++h)
     for (int d = 0; d < 3; ++d) win[h * 3 + d] = grid[d];
   sta::PlanHolder full;
   sta_status st = sta_plan_create(batch, heads, T, H, W, tile, win.data(), head_dim, &full.p);
   if (st != STA_OK) return st;
-  const int64_t plane = (int64_t)T * H * W * head_dim;
-  const size_t out_bytes = (size_t)batch * heads * plane * sizeof(float);
-  const size_t part_count = (size_t)batch * heads * sta::kRedBlocksPerPlane * 2;
+  int dev = -1;   // (after the argument checks, before any allocation on a device)
+  if (hipGetDevice(&dev) != hipSuccess) return STA_ERR_HIP;
   sta::DevBuf ref, cand, part;
-  if (hipMalloc(&ref.p, out_bytes) != hipSuccess || hipMalloc(&cand.p, out_bytes) != hipSuccess ||
+  if (sta::test_fail_alloc() || hipMalloc(&ref.p, out_bytes) != hipSuccess || hipMalloc(&cand.p, out_bytes) != hipSuccess ||
       hipMalloc(&part.p, part_count * sizeof(double)) != hipSuccess)
     return STA_ERR_ALLOC;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -123,7 +135,6 @@ sta_status sta_window_errors(const void *q, const void *k, const void *v, int ba
   st = sta_forward_plan(full.p, q, k, v, ref.p, scale, in_dtype, STA_F32, layout, stream);
   if (st != STA_OK) return fail(st);
 
-  std::vector<double> host(part_count);
   for (int c = 0; c < n_cand; ++c) {
     for (int h = 0; h < heads; ++h)
       for (int d = 0; d < 3; ++d) win[h * 3 + d] = candidates[c * 3 + d];
@@ -154,6 +165,38 @@ sta_status sta_window_errors(const void *q, const void *k, const void *v, int ba
     }
   }
   return STA_OK;
+}
+
+sta_status sta_window_search(const void *const *q, const void *const *k, const void *const *v,
+                             int n_samples, int batch, int heads, int T, int H, int W, const int tile[3],
+                             int head_dim, float scale, sta_dtype in_dtype, sta_layout layout,
+                             const int *candidates, int n_cand, double threshold, double *err_out,
+                             int *window_out, void *stream) {
+  if (!q || !k || !v || n_samples < 1 || !tile || !candidates || n_cand < 1 || heads < 1 || !window_out)
+    return STA_ERR_ARG;
+  for (int i = 0; i < n_samples; ++i)
+    if (!q[i] || !k[i] || !v[i]) return STA_ERR_ARG;
+  std::vector<double> one, mean;
+  try {
+    one.resize((size_t)heads * n_cand);
+    mean.assign((size_t)heads * n_cand, 0.0);
+  } catch (const std::bad_alloc &) {
+    return STA_ERR_ALLOC;
+  }
+  // W1, W2 per sample; W4: the arithmetic mean over the samples, summed in
+  // sample order
+  for (int i = 0; i < n_samples; ++i) {
+    const sta_status st = sta_window_errors(q[i], k[i], v[i], batch, heads, T, H, W, tile, head_dim, scale,
+                                            in_dtype, layout, candidates, n_cand, one.data(), stream);
+    if (st != STA_OK) return st;
+    for (size_t j = 0; j < one.size(); ++j) mean[j] += one[j];
+  }
+  for (double &x : mean) x /= n_samples;
+  if (err_out)
+    for (size_t j = 0; j < mean.size(); ++j) err_out[j] = mean[j];
+  // W3 on the mean (sta_window_errors checked that the extents are whole tiles)
+  const int grid[3] = {T / tile[0], H / tile[1], W / tile[2]};
+  return sta_window_select(heads, grid, candidates, n_cand, mean.data(), threshold, window_out);
 }
 
 }  // extern "C"

@@ -457,3 +457,36 @@ def test_swa_schedule_with_cost_sums_beyond_int32():
         q = full[x::8]
         q = q[q >= 0]
         assert np.all(np.diff(q) <= 0)
+
+
+# ---------------------------------------------------------------------------
+# Walk order of the key-tile lists (forward, dQ) and their inverses (dK/dV)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["720p", "mixed", "2d", "small"])
+def test_walk_order_is_residue_order(name):
+    """The kernels walk a window's key tiles in raster order of their
+    coordinates' residues modulo the window (one-to-one inside a window), and
+    a key tile's query tiles by the same residue, ties in raster order; both
+    lists hold exactly the tiles of the sorted queries."""
+    from oracle import sta_oracle as O
+    w = WORKLOADS[name]
+    plan = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    grid = O.tile_grid(w.video, w.tile)
+    coord = lambda t: (t // (grid[1] * grid[2]), (t // grid[2]) % grid[1], t % grid[2])
+    rng = np.random.default_rng(5)
+    n_tiles = grid[0] * grid[1] * grid[2]
+    for h in sorted(set(range(0, w.heads, max(1, w.heads // 6))) | {w.heads - 1}):
+        we = O.effective_window(w.windows[h], grid)
+        res = lambda t: tuple(c % e for c, e in zip(coord(t), we))
+        for t in sorted(set(rng.integers(0, n_tiles, size=12).tolist()) | {0, n_tiles - 1}):
+            walk = plan.walk(0, h, t)
+            assert sorted(walk) == plan.kv_tiles(h, t)
+            keys = [res(x) for x in walk]
+            assert keys == sorted(keys) and len(set(keys)) == len(keys), (h, t)
+            inv = plan.walk(1, h, t)
+            assert sorted(inv) == plan.q_tiles(h, t)
+            keys = [(res(x), x) for x in inv]
+            assert keys == sorted(keys), (h, t)
+    with pytest.raises(L.StaError):
+        plan.walk(2, 0, 0)

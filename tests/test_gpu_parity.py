@@ -265,7 +265,7 @@ def test_reference_max_overflow_repair():
     for h in range(w.heads):
         for c in tiles:
             qt = (c[0] * grid[1] + c[1]) * grid[2] + c[2]
-            first = plan.kv_tiles(h, qt)[0]
+            first = plan.walk(0, h, qt)[0]
             fc = (first // (grid[1] * grid[2]), (first // grid[2]) % grid[1], first % grid[2])
             qs = qf[h][tile_slice(w, c)].reshape(-1, w.head_dim).astype(np.float64)
             ks_first = kf[h][tile_slice(w, fc)].reshape(-1, w.head_dim)[:32].astype(np.float64)

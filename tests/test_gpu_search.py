@@ -70,10 +70,28 @@ def test_window_errors_and_choice():
 
 
 def test_window_search_averages_samples():
-    say("case window search over two calibration samples")
-    samples = [tuple(x.cuda() for x in _inputs(s)) for s in (21, 22)]
+    """sta_window_search over three calibration samples against the oracle's
+    W1-W4 (per-sample errors, their mean, the choice from the mean)."""
+    say("case window search over three calibration samples")
+    samples = [_inputs(s) for s in (21, 22, 23)]
     cands = api.window_candidates(GRID)
-    windows, mean, _ = api.window_search(samples, TILE, 0.1)
-    each = [api.window_errors(*s, TILE, cands) for s in samples]
-    assert np.array_equal(mean, (each[0] + each[1]) / 2)
-    assert windows == api.window_select(mean, cands, GRID, 0.1)
+    N = VIDEO[0] * VIDEO[1] * VIDEO[2]
+    ref_samples = [tuple(x.reshape(1, 4, N, D).double().numpy() for x in s) for s in samples]
+    for tau in (0.02, 0.1, 0.3):
+        windows, mean, got_cands = api.window_search([tuple(x.cuda() for x in s) for s in samples], TILE, tau)
+        assert got_cands == [tuple(c) for c in cands]
+        want, ref = OS.search(ref_samples, VIDEO, TILE, cands, tau, scale=1.0 / 8)
+        d = np.abs(mean - ref)
+        say(f"  tau {tau}: max |mean_gpu - mean_oracle| {d.max():.2e}; {windows}")
+        assert (d <= tol(ref)).all()
+        assert (mean[:, cands.index(GRID)] == 0).all()
+        for h in range(4):
+            if windows[h] == want[h]:
+                continue
+            lo, hi = ref[h] - tol(ref[h]), ref[h] + tol(ref[h])
+            ok_lo = OS.select_windows(lo[None], cands, GRID, tau)[0]
+            ok_hi = OS.select_windows(hi[None], cands, GRID, tau)[0]
+            assert windows[h] in (ok_lo, ok_hi), (h, tau, windows[h], want[h])
+        # the library's mean is the mean of its own per-sample errors
+        each = [api.window_errors(*(x.cuda() for x in s), TILE, cands) for s in samples]
+        assert np.allclose(mean, (each[0] + each[1] + each[2]) / 3, rtol=1e-15, atol=0)

@@ -56,3 +56,21 @@ def test_plan_released_right_after_launch():
     del tmp                         # sta_plan_destroy waits for the queued work first
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+def test_tables_uploaded_on_one_stream_are_awaited_by_another():
+    print("case small workload: tables uploaded behind a spin on stream 1, first used on stream 2",
+          file=sys.stderr, flush=True)
+    w = WORKLOADS["small"]
+    keep = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    q, k, v = (x.cuda() for x in make_qkv(w))
+    ref = api.sta_forward_plan(keep, q, k, v, scale=w.scale)
+    torch.cuda.synchronize()
+    plan = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        torch.cuda._sleep(50_000_000)   # a bounded spin: the upload below queues behind it
+    out1 = api.sta_forward_plan(plan, q, k, v, scale=w.scale, stream=s1)   # uploads the tables on s1
+    out2 = api.sta_forward_plan(plan, q, k, v, scale=w.scale, stream=s2)   # must wait for that upload
+    torch.cuda.synchronize()
+    assert torch.equal(out1, ref) and torch.equal(out2, ref)

@@ -138,8 +138,35 @@ def pin_choice_constraints(mod, seed=5):
     return fails
 
 
+def pin_search_over_samples(mod, seed=6):
+    # W4 by its properties: one sample gives that sample's errors; a sample
+    # given twice changes nothing; the order of the samples does not matter;
+    # every mean lies between the samples' errors; the choice is W3 on it.
+    rng = np.random.default_rng(seed)
+    s1, s2 = _rand(rng), tuple(2.0 * x for x in _rand(rng))
+    cands = S.odd_candidates(GRID) + [(1, 2, 1)]
+    e1 = mod.window_errors(*s1, VIDEO, TILE, cands, scale=0.4)
+    e2 = mod.window_errors(*s2, VIDEO, TILE, cands, scale=0.4)
+    fails = []
+    w1, m1 = mod.search([s1], VIDEO, TILE, cands, 0.3, scale=0.4)
+    if not np.array_equal(m1, e1):
+        fails.append(("one sample", float(np.abs(m1 - e1).max())))
+    _, m11 = mod.search([s1, s1], VIDEO, TILE, cands, 0.3, scale=0.4)
+    if not np.array_equal(m11, e1):
+        fails.append(("duplicate sample", float(np.abs(m11 - e1).max())))
+    w12, m12 = mod.search([s1, s2], VIDEO, TILE, cands, 0.3, scale=0.4)
+    _, m21 = mod.search([s2, s1], VIDEO, TILE, cands, 0.3, scale=0.4)
+    if not np.array_equal(m12, m21):
+        fails.append(("sample order", float(np.abs(m12 - m21).max())))
+    if not ((m12 >= np.minimum(e1, e2)) & (m12 <= np.maximum(e1, e2))).all() or np.array_equal(e1, e2):
+        fails.append(("mean outside the samples' errors",))
+    if w12 != mod.select_windows(m12, cands, GRID, 0.3) or w1 != mod.select_windows(e1, cands, GRID, 0.3):
+        fails.append(("choice", w12))
+    return fails
+
+
 ALL_PINS = [pin_full_window_is_exact, pin_constant_v, pin_tile_confined_attention,
-            pin_error_against_dense_library, pin_choice_constraints]
+            pin_error_against_dense_library, pin_choice_constraints, pin_search_over_samples]
 
 
 def run_pins(mod):
@@ -173,6 +200,8 @@ MUTANTS = [
     ("fallback to the last candidate", "out.append(best[1] if best is not None else tuple(int(n) for n in grid))",
      "out.append(best[1] if best is not None else tuple(candidates[-1]))"),
     ("strict threshold", "if not err[h, c] <= threshold:", "if not err[h, c] < threshold:"),
+    ("sum of the samples, not their mean", "    mean /= len(errs)\n", "    pass\n"),
+    ("last sample only", "        mean += e\n", "        mean = e.copy()\n"),
     ("dense reference with a 3-tile window",
      "full = F.sta_forward_explicit(q, k, v, video, tile, [grid] * heads, scale=scale)",
      "full = F.sta_forward_explicit(q, k, v, video, tile, [(3, 3, 3)] * heads, scale=scale)"),
