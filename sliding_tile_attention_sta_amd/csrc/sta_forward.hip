@@ -469,8 +469,15 @@ next_item:
   };
   // Softmax of one block.  The new row sums are checked before they replace
   // l: an overflowed probability makes its row sum +inf, and then the wave
-  // repairs the block (reference moved to the row max, O and l rescaled,
-  // probabilities recomputed, now <= 1).  O is in VGPRs, so the rescale
+  // repairs the block: every row's reference rises to 2^4 (exp2 units)
+  // above the row's max so far unless it is higher already, O and l are
+  // rescaled and the block's probabilities recomputed (a row whose reference
+  // moved now has them all <= 2^-4).  The headroom lets a row's max grow by
+  // 2^20 instead of 2^16 before the next repair: on inputs whose
+  // rows' maxima keep growing along the walk (per-token magnitudes up to 4)
+  // it removes a fifth of the repairs, each of which holds the work group
+  // at the step's barrier, and keeps the probabilities within fp16's normal
+  // range relative to the row's largest.  O is in VGPRs, so the rescale
   // needs no register copies.
   auto softmax = [&]() {
     float ln[QB];
@@ -485,7 +492,7 @@ next_item:
     if (__builtin_amdgcn_ballot_w64(!(lmax <= 3.0e38f))) {
 #pragma unroll
       for (int j = 0; j < QB; ++j) {
-        const float mnew = fmaxf(m[j], swap_max(lane_max(j)));
+        const float mnew = fmaxf(m[j], swap_max(lane_max(j)) + 4.f / sl2e);
         const float alpha = __builtin_amdgcn_exp2f((m[j] - mnew) * sl2e);
         m[j] = mnew;
         mb[j] = mnew * sl2e;
