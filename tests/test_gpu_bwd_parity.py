@@ -239,3 +239,42 @@ def test_long_stress_sampled():
     w = WORKLOADS["long"]
     say("case long backward: 60x48x80, per-token magnitude U(0.5, 4)")
     _sampled(w, heads=(7,), n_query=4, n_key=3)
+
+
+# ---------------------------------------------------------------------------
+# fp32 inputs against the unrounded definition
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "generic-d128-f32"])
+def test_fp32_backward_against_unrounded_inputs(name):
+    """The fp32 backward computes with q, k rounded to bf16 and v, dout to
+    fp16 (the header's contract).  Against the gradients of the UNROUNDED
+    fp32 inputs its error is bounded by the triangle inequality:
+        |gpu - exact| <= |gpu - exact(rounded inputs)| + |exact(rounded) - exact|
+    the first term by the kernels' parity bound (2e-2 max, 2e-3 mean, of the
+    gradient's rms), the second computed here by the float64 oracle on both
+    input sets (the cost of the input rounding alone).  Both are reported."""
+    w = WORKLOADS[name]
+    say(f"case {name}: fp32 backward against the unrounded inputs")
+    q, k, v = make_qkv(w)
+    g = make_grad_out(w)
+    assert q.dtype == torch.float32
+    _, out, lse, dq, dk, dv = run_bwd(w, q.cuda(), k.cuda(), v.cuda(), g.cuda())
+    qr, kr, vr, gr = consumed(q, k, v, g)
+    for h in range(w.heads):
+        sl = slice(h, h + 1)
+        exact = OB.sta_backward_explicit(*(flat(x, w)[:, sl].double().numpy() for x in (q, k, v, g)),
+                                         w.video, w.tile, [w.windows[h]], scale=w.scale)
+        rounded = OB.sta_backward_explicit(*(flat(x, w)[:, sl].double().numpy() for x in (qr, kr, vr, gr)),
+                                           w.video, w.tile, [w.windows[h]], scale=w.scale)
+        for nm, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            got = flat(t, w)[:, sl].double().cpu().numpy()
+            rms = float(np.sqrt(np.mean(exact[nm] ** 2)))
+            e_round = np.abs(rounded[nm] - exact[nm]) / rms
+            e_gpu = np.abs(got - exact[nm]) / rms
+            say(f"  head {h} {nm}: input rounding alone max/rms {e_round.max():.2e} mean/rms "
+                f"{e_round.mean():.2e}; gpu vs unrounded max/rms {e_gpu.max():.2e} mean/rms {e_gpu.mean():.2e}")
+            # (the parity bound is relative to the rounded-input gradient's rms)
+            rr = float(np.sqrt(np.mean(rounded[nm] ** 2))) / rms
+            assert e_gpu.max() <= e_round.max() + MAX_REL * rr, nm
+            assert e_gpu.mean() <= e_round.mean() + MEAN_REL * rr, nm
