@@ -135,24 +135,36 @@ sta_status sta_window_errors(const void *q, const void *k, const void *v, int ba
   st = sta_forward_plan(full.p, q, k, v, ref.p, scale, in_dtype, STA_F32, layout, stream);
   if (st != STA_OK) return fail(st);
 
+  // Candidate c's plan is built on the host while the GPU runs candidate
+  // c - 1 (two plans alive at a time); a plan goes once the stream has
+  // drained after its launches.
+  sta::PlanHolder cp[2];
+  auto make = [&](int c, sta::PlanHolder &h) {
+    for (int hh = 0; hh < heads; ++hh)
+      for (int d = 0; d < 3; ++d) win[hh * 3 + d] = candidates[c * 3 + d];
+    return sta_plan_create(batch, heads, T, H, W, tile, win.data(), head_dim, &h.p);
+  };
+  st = make(0, cp[0]);
+  if (st != STA_OK) return fail(st);
   for (int c = 0; c < n_cand; ++c) {
-    for (int h = 0; h < heads; ++h)
-      for (int d = 0; d < 3; ++d) win[h * 3 + d] = candidates[c * 3 + d];
-    sta::PlanHolder cp;
-    st = sta_plan_create(batch, heads, T, H, W, tile, win.data(), head_dim, &cp.p);
-    if (st != STA_OK) return fail(st);
-    st = sta_forward_plan(cp.p, q, k, v, cand.p, scale, in_dtype, STA_F32, layout, stream);
+    sta::PlanHolder &cur = cp[c & 1], &nxt = cp[(c + 1) & 1];
+    st = sta_forward_plan(cur.p, q, k, v, cand.p, scale, in_dtype, STA_F32, layout, stream);
     if (st != STA_OK) return fail(st);
     hipLaunchKernelGGL(sta::sq_diff_kernel, dim3(sta::kRedBlocksPerPlane, batch * heads),
                        dim3(sta::kRedThreads), 0, s, static_cast<const float *>(cand.p),
                        static_cast<const float *>(ref.p), static_cast<double *>(part.p), plane);
     if (hipGetLastError() != hipSuccess) return fail(STA_ERR_HIP);
+    // (before the copy: a copy into pageable host memory may block the host)
+    if (c + 1 < n_cand) {
+      st = make(c + 1, nxt);
+      if (st != STA_OK) return fail(st);
+    }
     if (hipMemcpyAsync(host.data(), part.p, part_count * sizeof(double), hipMemcpyDeviceToHost, s) !=
             hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
       return fail(STA_ERR_HIP);
-    // The plan's device tables were used by the launch above; the stream
-    // has drained, so the plan may go.
+    sta_plan_destroy(cur.p);
+    cur.p = nullptr;
     for (int h = 0; h < heads; ++h) {
       double sd = 0.0, sr = 0.0;
       for (int b = 0; b < batch; ++b)
