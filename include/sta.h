@@ -381,6 +381,17 @@ sta_status sta_window_candidates(const int grid[3], int *out, int cap, int *coun
  * plan that a call is still using is destroyed when that call returns. */
 sta_status sta_clear_plan_cache(void);
 
+/* Debug builds only (libsta_debug.so, compiled with -DSTA_DEBUG): the
+ * kernels check work item codes, tile-list entries, token rows, buffer
+ * offsets and LDS table indices, and a failed check sets a bit in a word on
+ * the current device instead of trapping (bits: 0 work item or piece,
+ * 1 tile-list entry, 2 row or offset of a load, 3 row of a store, 4 LDS
+ * table index).  *flags receives the word (after the work queued before the
+ * call on the null stream has finished); clear != 0 resets it.  Release
+ * builds: *flags = 0 and STA_ERR_UNSUPPORTED.  STA_ERR_ARG for a NULL
+ * flags, STA_ERR_HIP if the device cannot be read. */
+sta_status sta_debug_flags(uint32_t *flags, int clear);
+
 /* Static, human-readable name of a status code. */
 const char *sta_status_string(sta_status status);
 

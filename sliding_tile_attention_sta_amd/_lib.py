@@ -10,6 +10,8 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsta.so")
+# The same library built with the kernels' bounds checks (-DSTA_DEBUG).
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsta_debug.so")
 
 STA_OK, STA_ERR_ARG, STA_ERR_SHAPE, STA_ERR_UNSUPPORTED, STA_ERR_ALLOC, STA_ERR_HIP = 0, -1, -2, -3, -4, -5
 STA_BF16, STA_F32 = 0, 1
@@ -53,6 +55,7 @@ SIGNATURES = {
     "sta_plan_pieces": (_I, [_P, _I32P, _I64, ctypes.POINTER(_I64)]),
     "sta_plan_q_tiles": (_I, [_P, _I, _I, _I32P, _I, _IP]),
     "sta_plan_walk": (_I, [_P, _I, _I, _I, _I32P, _I, _IP]),
+    "sta_debug_flags": (_I, [ctypes.POINTER(ctypes.c_uint32), _I]),
     "sta_plan_schedule_bwd": (_I, [_P, _I, _I32P, _I64, ctypes.POINTER(_I64)]),
     "sta_tile_reorder": (_I, [_P, _P, _P, _I, _P]),
     "sta_tile_unreorder": (_I, [_P, _P, _P, _I, _P]),
@@ -83,19 +86,35 @@ class StaError(RuntimeError):
         super().__init__(f"{where}: {status_string(status)}")
 
 
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m sliding_tile_attention_sta_amd.build`")
+    l = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(l, name)
+        f.restype = res
+        f.argtypes = args
+    return l
+
+
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -m sliding_tile_attention_sta_amd.build`")
-        l = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            f = getattr(l, name)
-            f.restype = res
-            f.argtypes = args
-        _lib = l
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+_debug_lib = None
+
+
+def debug_lib() -> ctypes.CDLL:
+    """libsta_debug.so: the same entry points with bounds-checked kernels
+    (read the violations with sta_debug_flags)."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(DEBUG_LIB_PATH)
+    return _debug_lib
 
 
 def status_string(status: int) -> str:

@@ -23,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsta.so")
+LIB_DEBUG = os.path.join(PKG, "libsta_debug.so")   # the kernels' bounds checks on (-DSTA_DEBUG)
 
 HIP_SOURCES = ["sta_api.hip", "sta_forward.hip", "sta_backward.hip", "sta_reorder.hip", "sta_search.hip"]
 # Per-file extra flags.  The forward kernel needs no IEEE signalling-NaN
@@ -58,18 +59,21 @@ def _run(cmd):
     return r.stdout
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
+def build(jobs: int | None = None, verbose: bool = False, debug: bool = False) -> str:
+    """Compile the library (debug: libsta_debug.so, with -DSTA_DEBUG)."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD, exist_ok=True)
+    bdir = BUILD + ("_debug" if debug else "")
+    os.makedirs(bdir, exist_ok=True)
+    extra = ["-DSTA_DEBUG"] if debug else []
     cmds, objs = [], []
     for s in HIP_SOURCES:
-        o = os.path.join(BUILD, s + ".o")
-        cmds.append([HIPCC, *HIP_FLAGS, *HIP_EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o])
+        o = os.path.join(bdir, s + ".o")
+        cmds.append([HIPCC, *HIP_FLAGS, *HIP_EXTRA.get(s, []), *extra, "-c", os.path.join(CSRC, s), "-o", o])
         objs.append(o)
     for s in CXX_SOURCES:
-        o = os.path.join(BUILD, s + ".o")
-        cmds.append([CXX, *CXX_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
+        o = os.path.join(bdir, s + ".o")
+        cmds.append([CXX, *CXX_FLAGS, *extra, "-c", os.path.join(CSRC, s), "-o", o])
         objs.append(o)
     jobs = jobs or min(8, len(cmds))
     with ThreadPoolExecutor(jobs) as ex:
@@ -79,18 +83,20 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
             print(" ".join(c))
             if o.strip():
                 print(o)
-    tmp = LIB + ".tmp"
+    out = LIB_DEBUG if debug else LIB
+    tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--debug", action="store_true", help="build libsta_debug.so (kernel bounds checks)")
     args = ap.parse_args(argv)
-    print(build(args.jobs, args.verbose))
+    print(build(args.jobs, args.verbose, args.debug))
 
 
 if __name__ == "__main__":

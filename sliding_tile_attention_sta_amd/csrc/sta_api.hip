@@ -141,6 +141,26 @@ sta_status static_scratch(void **out) {
   return STA_OK;
 }
 
+// Debug builds: one word per device that the kernels' bounds checks set
+// bits in (see STA_CHECK), at a device address looked up once per device.
+#ifdef STA_DEBUG
+static __device__ unsigned dbg_word;
+unsigned *g_dbg_ptr[kMaxDevices] = {};
+unsigned *debug_word() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_dbg_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(dbg_word)) != hipSuccess) return nullptr;
+    g_dbg_ptr[dev] = static_cast<unsigned *>(ptr);
+  }
+  return g_dbg_ptr[dev];
+}
+#else
+unsigned *debug_word() { return nullptr; }
+#endif
+
 // The forward scratch of a plan with dynamic queues on the current device,
 // for launches on `stream` (allocated on first use; its counters are
 // cleared once, in stream order, and every launch leaves them zero).
@@ -325,6 +345,9 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   a.pslot = p->n_pieces ? reinterpret_cast<float *>(static_cast<char *>(scratch) +
                                                     fwd_counter_bytes(p->n_groups, p->items()))
                         : nullptr;
+  a.n_items = (int32_t)p->items();
+  a.n_pieces = p->n_pieces;
+  a.dbg = debug_word();
   hipError_t e = sta::launch_forward(a, p->variant, p->D, in_dtype == STA_F32, out_dtype == STA_F32,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? STA_OK : STA_ERR_HIP;
@@ -381,6 +404,8 @@ sta_status backward(const sta_plan *p, const void *q, const void *k, const void 
   a.list_idx = t.kv_idx;
   a.max_list = p->max_nkv;
   a.subs = p->bwd_q_subs;
+  a.n_items = p->batch * p->heads * p->n_tiles * p->bwd_q_subs;
+  a.dbg = debug_word();
   if (launch_bwd_dq(a, p->bwd_q_waves, p->D, f32_in, s) != hipSuccess) return STA_ERR_HIP;
   a.sched = t.sched_dkdv;
   a.n_blocks = (int32_t)p->sched_dkdv.size();
@@ -388,6 +413,7 @@ sta_status backward(const sta_plan *p, const void *q, const void *k, const void 
   a.list_idx = t.q_idx;
   a.max_list = p->max_nq;
   a.subs = p->bwd_k_subs;
+  a.n_items = p->batch * p->heads * p->n_tiles * p->bwd_k_subs;
   if (launch_bwd_dkdv(a, p->bwd_k_pairs, p->D, f32_in, s) != hipSuccess) return STA_ERR_HIP;
   return STA_OK;
 }
@@ -433,6 +459,24 @@ sta_status sta_forward(const void *q, const void *k, const void *v, void *out, i
   const std::shared_ptr<sta_plan> p = sta::cached_plan(batch, heads, T, H, W, tile, window, head_dim, &st);
   if (!p) return st;
   return sta_forward_plan(p.get(), q, k, v, out, scale, in_dtype, out_dtype, layout, stream);
+}
+
+sta_status sta_debug_flags(uint32_t *flags, int clear) {
+  if (!flags) return STA_ERR_ARG;
+  *flags = 0;
+#ifdef STA_DEBUG
+  unsigned *w = sta::debug_word();
+  if (!w) return STA_ERR_HIP;
+  if (hipMemcpy(flags, w, sizeof(unsigned), hipMemcpyDeviceToHost) != hipSuccess) return STA_ERR_HIP;
+  if (clear) {
+    const unsigned zero = 0;
+    if (hipMemcpy(w, &zero, sizeof(unsigned), hipMemcpyHostToDevice) != hipSuccess) return STA_ERR_HIP;
+  }
+  return STA_OK;
+#else
+  (void)clear;
+  return STA_ERR_UNSUPPORTED;
+#endif
 }
 
 }  // extern "C"

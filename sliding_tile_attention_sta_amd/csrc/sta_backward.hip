@@ -185,6 +185,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
 
   const int item = __builtin_amdgcn_readfirstlane(a.sched[blockIdx.x]);
   if (item < 0) return;
+  STA_CHECK(a.dbg, item < a.n_items, 0);
   const Item it = decode(item, a);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -192,7 +193,10 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
   const int l0 = __builtin_amdgcn_readfirstlane(a.list_off[it.h * a.n_tiles + it.tile]);
   const int nl = __builtin_amdgcn_readfirstlane(a.list_off[it.h * a.n_tiles + it.tile + 1]) - l0;
   for (int i = tid; i < a.V; i += NT) off_l[i] = a.off[i];
-  for (int i = tid; i < nl; i += NT) lb_l[i] = a.base[a.list_idx[l0 + i]];
+  for (int i = tid; i < nl; i += NT) {
+    STA_CHECK(a.dbg, (unsigned)a.list_idx[l0 + i] < (unsigned)a.n_tiles && i < a.max_list, 1);
+    lb_l[i] = a.base[a.list_idx[l0 + i]];
+  }
 
   const size_t plane = (size_t)it.bh * a.N;
   const char *qg = static_cast<const char *>(a.q) + plane * D * EB;
@@ -211,6 +215,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = qbase + off_l[qloc0 + 16 * j + l16];
+    STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 2);
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       const size_t e = (size_t)row * D + 32 * c + 8 * g;
@@ -236,6 +241,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (CHUNKS < NT && c >= CHUNKS) break;
+      STA_CHECK(a.dbg, (unsigned)(tb + off_l[u * TB + c / (D / 8)]) < (unsigned)a.N, 2);
       const size_t e = (size_t)(tb + off_l[u * TB + c / (D / 8)]) * D + (c % (D / 8)) * 8;
       dk[i] = load_raw<F32IN>(kg + e * EB);
       dv[i] = load_raw<F32IN>(vg + e * EB);
@@ -335,6 +341,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = qbase + off_l[qloc0 + 16 * j + l16];
+    STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 3);
 #pragma unroll
     for (int b = 0; b < DB; ++b) store4(dq, (size_t)row * D + 16 * b + 4 * g, acc[b][j] * a.scale, a.f32_out);
   }
@@ -381,6 +388,7 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
 
   const int item = __builtin_amdgcn_readfirstlane(a.sched[blockIdx.x]);
   if (item < 0) return;
+  STA_CHECK(a.dbg, item < a.n_items, 0);
   const Item it = decode(item, a);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -390,7 +398,10 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
   const int l0 = __builtin_amdgcn_readfirstlane(a.list_off[it.h * a.n_tiles + it.tile]);
   const int nl = __builtin_amdgcn_readfirstlane(a.list_off[it.h * a.n_tiles + it.tile + 1]) - l0;
   for (int i = tid; i < a.V; i += NT) off_l[i] = a.off[i];
-  for (int i = tid; i < nl; i += NT) lb_l[i] = a.base[a.list_idx[l0 + i]];
+  for (int i = tid; i < nl; i += NT) {
+    STA_CHECK(a.dbg, (unsigned)a.list_idx[l0 + i] < (unsigned)a.n_tiles && i < a.max_list, 1);
+    lb_l[i] = a.base[a.list_idx[l0 + i]];
+  }
 
   const size_t plane = (size_t)it.bh * a.N;
   const char *qg = static_cast<const char *>(a.q) + plane * D * EB;
@@ -408,6 +419,7 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int row = kbase + off_l[kloc0 + 16 * kb + l16];
+      STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 2);
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         const Raw8<F32IN> r = load_raw<F32IN>(src + ((size_t)row * D + 32 * c + 8 * g) * EB);
@@ -429,12 +441,14 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (CHUNKS < NT && c >= CHUNKS) break;
+      STA_CHECK(a.dbg, (unsigned)(tb + off_l[u * TB + c / (D / 8)]) < (unsigned)a.N, 2);
       const size_t e = (size_t)(tb + off_l[u * TB + c / (D / 8)]) * D + (c % (D / 8)) * 8;
       rq[i] = load_raw<F32IN>(qg + e * EB);
       rg[i] = load_raw<F32IN>(gg + e * EB);
     }
     if (tid < 2 * TB) {
       const int row = tb + off_l[u * TB + (tid & (TB - 1))];
+      STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 2);
       rs = tid < TB ? lse[row] * kLog2e : delta[row];
     }
   };
@@ -545,6 +559,7 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int row = kbase + off_l[kloc0 + 16 * kb + l16];
+    STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 3);
 #pragma unroll
     for (int b = 0; b < DB; ++b) store4(dst, (size_t)row * D + 16 * b + 4 * g, acc[b][kb] * mul, a.f32_out);
   }

@@ -6,6 +6,22 @@
 
 #include <cstdint>
 
+// Debug builds (-DSTA_DEBUG, libsta_debug.so): bounds checks on work item
+// codes, table entries, token rows and buffer offsets.  A failed check sets
+// a bit in a device word (read back by sta_debug_flags) instead of
+// trapping, so that a test reports it without faulting the GPU.  Bits:
+// 0 work item or piece, 1 tile-list entry, 2 row or offset of a load,
+// 3 row of a store, 4 LDS table index.  Release builds compile the checks
+// away.
+#ifdef STA_DEBUG
+#define STA_CHECK(dbg, cond, bit)                                   \
+  do {                                                              \
+    if (!(cond)) __hip_atomic_fetch_or((dbg), 1u << (bit), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); \
+  } while (0)
+#else
+#define STA_CHECK(dbg, cond, bit) ((void)0)
+#endif
+
 namespace sta {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

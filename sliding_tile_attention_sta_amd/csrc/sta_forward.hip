@@ -194,10 +194,12 @@ next_item:
   int piece = -1, s_first = 0, s_end = 0;
   if (item < -1) {
     piece = -2 - item;
+    STA_CHECK(a.dbg, piece < a.n_pieces, 0);
     item = __builtin_amdgcn_readfirstlane(a.ptab[4 * piece]);
     s_first = __builtin_amdgcn_readfirstlane(a.ptab[4 * piece + 1]);
     s_end = __builtin_amdgcn_readfirstlane(a.ptab[4 * piece + 2]);
   }
+  STA_CHECK(a.dbg, item >= 0 && item < a.n_items, 0);
   const int sub = item % a.subs;
   const int rest = item / a.subs;
   const int qt = rest % a.n_tiles;
@@ -212,7 +214,10 @@ next_item:
     nkv = __builtin_amdgcn_readfirstlane(a.kv_off[h * a.n_tiles + qt + 1]) - kv0;
   }
   for (int i = tid; i < a.V; i += NT) off_l[i] = a.off[i];
-  for (int i = tid; i < nkv; i += NT) kvb_l[i] = a.base[a.kv_idx[kv0 + i]];
+  for (int i = tid; i < nkv; i += NT) {
+    STA_CHECK(a.dbg, (unsigned)a.kv_idx[kv0 + i] < (unsigned)a.n_tiles && i < a.max_nkv, 1);
+    kvb_l[i] = a.base[a.kv_idx[kv0 + i]];
+  }
   // SWA: the union box of the tile's query windows, walked as rows (t, y)
   // of nzb runs of 32 keys starting at z = z_lo.
   int s_wt = 0, s_wy = 0, s_wz = 0, s_tlo = 0, s_ylo = 0, s_zlo = 0, s_ny = 1, s_nzb = 1, s_nrows = 0;
@@ -258,6 +263,7 @@ next_item:
   for (int j = 0; j < QB; ++j) {
     int row = qbase + off_l[qloc0 + 16 * j + l16];
     if constexpr (PARTIAL) row = row < a.N ? row : (int)a.N - 1;
+    STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N && qloc0 + 16 * j + l16 < a.V, 2);
 #pragma unroll
     for (int c = 0; c < DC; ++c)
       qf[j][c] = __builtin_bit_cast(bf16x8, as_bf16<F32IN>(load_raw<F32IN>(
@@ -289,6 +295,7 @@ next_item:
         if (CHUNKS < NT && c >= CHUNKS) break;
         const int z = z0 + c / (D / 8);
         nrow[i] = r0 + (z < a.W ? z : a.W - 1);
+        STA_CHECK(a.dbg, (unsigned)nrow[i] < (unsigned)a.N, 2);
       }
       return;
     }
@@ -299,6 +306,8 @@ next_item:
       if (CHUNKS < NT && c >= CHUNKS) break;
       nrow[i] = tb + off_l[u * KB + c / (D / 8)];
       if constexpr (PARTIAL) nrow[i] = nrow[i] < a.N ? nrow[i] : (int)a.N - 1;
+      STA_CHECK(a.dbg, (unsigned)nrow[i] < (unsigned)a.N, 2);
+      STA_CHECK(a.dbg, u * KB + c / (D / 8) < a.V, 4);
     }
   };
   // SEP: a 32-key block is read with buffer loads at a per-lane constant
@@ -326,6 +335,7 @@ next_item:
       for (int i = 0; i < CPT; ++i) {
         const int c = tid + i * NT;
         if (CHUNKS < NT && c >= CHUNKS) break;
+        STA_CHECK(a.dbg, nrow[0] >= 0 && (long long)nrow[0] + voff[i] + 8 * EB <= a.N * D * EB, 2);
         if constexpr (F32IN) {
           dst[i].x = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + nrow[0], 0, 0));
           dst[i].y = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + nrow[0] + 16, 0, 0));
@@ -804,6 +814,7 @@ next_item:
       const int ql = qloc0 + 16 * j + l16;
       if (!((a.kmask[(size_t)qt * spt + ql / 32] >> (ql % 32)) & 1u)) continue;
     }
+    STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 3);
     if (a.lse != nullptr && g == 0)
       a.lse[(size_t)bh * a.N + row] = (mb[j] + log2f(lsum)) * 0.69314718055994530942f;
 #pragma unroll

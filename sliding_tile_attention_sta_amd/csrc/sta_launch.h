@@ -47,6 +47,8 @@ struct FwdArgs {
   const int32_t *gtab;
   int32_t *pcount;
   float *pslot;
+  int32_t n_items, n_pieces;   // item codes in [0, n_items), pieces in [0, n_pieces)
+  unsigned *dbg;               // debug builds: bounds-check violation bits (else unused)
 };
 
 // Zero n int32 (a fill kernel, so that the clear can sit in a captured graph).
@@ -73,6 +75,8 @@ struct BwdArgs {
   int32_t n_blocks;        // length of sched
   int32_t max_list;        // longest list
   int32_t f32_out;         // gradients stored as fp32 (else bf16)
+  int32_t n_items;         // work item codes in [0, n_items)
+  unsigned *dbg;           // debug builds: bounds-check violation bits (else unused)
 };
 
 // delta[r] = sum_d dO[r, d] * O[r, d] for rows r < rows.
