@@ -190,9 +190,23 @@ sta_status sta_plan_q_tiles(const sta_plan *plan, int head, int kv_tile, int32_t
  * (info.kernel_variant 1) the queues are consumed dynamically: each work
  * group takes the next entry of its own XCD's queue, or, once that queue
  * is empty, of another's, so a faster XCD takes more of the work; otherwise
- * work group b runs entry b.  out: host buffer of cap int32; *count
- * receives the entry count (STA_ERR_ARG if it exceeds cap). */
+ * work group b runs entry b.  Plans of the 384-query kernel with fewer
+ * work items than the chip's 256 compute units may instead cut the
+ * launch's key steps into one contiguous range per work group (see
+ * sta_plan_group_lists): the schedule is then the groups' lists,
+ * concatenated.  out: host buffer of cap int32; *count receives the entry
+ * count (STA_ERR_ARG if it exceeds cap). */
 sta_status sta_plan_schedule(const sta_plan *plan, int32_t *out, int64_t cap, int64_t *count);
+
+/* Per-work-group lists of the forward (plans with fewer work items than
+ * compute units, where balancing the units' key steps pays): work group b
+ * runs the schedule's entries off[b] .. off[b + 1] - 1 in turn, whole items
+ * and pieces (see sta_plan_pieces) that together walk one contiguous range
+ * of the launch's key steps, the items taken in decreasing-cost order.
+ * out: host buffer of cap int32 that receives info.launch_blocks + 1
+ * offsets; *count receives that number, or 0 when the plan has no such
+ * lists (STA_ERR_ARG if it exceeds cap). */
+sta_status sta_plan_group_lists(const sta_plan *plan, int32_t *out, int64_t cap, int64_t *count);
 
 /* The pieces of split work items (info.pieces of them).  A work item of the
  * forward walks its key tiles' 32-key blocks in order, steps

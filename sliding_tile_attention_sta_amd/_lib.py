@@ -53,6 +53,7 @@ SIGNATURES = {
     "sta_plan_kv_tiles": (_I, [_P, _I, _I, _I32P, _I, _IP]),
     "sta_plan_schedule": (_I, [_P, _I32P, _I64, ctypes.POINTER(_I64)]),
     "sta_plan_pieces": (_I, [_P, _I32P, _I64, ctypes.POINTER(_I64)]),
+    "sta_plan_group_lists": (_I, [_P, _I32P, _I64, ctypes.POINTER(_I64)]),
     "sta_plan_q_tiles": (_I, [_P, _I, _I, _I32P, _I, _IP]),
     "sta_plan_walk": (_I, [_P, _I, _I, _I, _I32P, _I, _IP]),
     "sta_debug_flags": (_I, [ctypes.POINTER(ctypes.c_uint32), _I]),

@@ -171,6 +171,16 @@ class Plan:
                                         ctypes.byref(n)), "sta_plan_pieces")
         return out[:n.value]
 
+    def group_lists(self) -> torch.Tensor:
+        """Offsets of the per-work-group lists into schedule() (launch_blocks
+        + 1 of them), or an empty tensor when the forward uses queues."""
+        n = ctypes.c_int64()
+        L.lib().sta_plan_group_lists(self._h, None, 0, ctypes.byref(n))
+        out = torch.empty(max(1, n.value), dtype=torch.int32)
+        L.check(L.lib().sta_plan_group_lists(self._h, ctypes.cast(out.data_ptr(), L._I32P), n.value,
+                                             ctypes.byref(n)), "sta_plan_group_lists")
+        return out[:n.value]
+
 
 def sta_plan_create(batch, heads, video, tile, windows, head_dim) -> Plan:
     return Plan(batch, heads, video, tile, windows, head_dim)

@@ -44,7 +44,8 @@ sta_status device_tables(const sta_plan *p, void *stream, DeviceTables *out) {
   const std::vector<int32_t> *parts[] = {&p->kv_off, &p->kv_idx,   &p->sched,    &p->base_nat,
                                          &p->off_nat, &p->base_tm,  &p->off_tm,   &p->q_off,
                                          &p->q_idx,   &p->sched_dq, &p->sched_dkdv, &p->kmask,
-                                         &p->swin,    &p->ptab,     &p->gtab,     &p->queue};
+                                         &p->swin,    &p->ptab,     &p->gtab,     &p->queue,
+                                         &p->wlist,   &p->woff};
   constexpr int kParts = sizeof(parts) / sizeof(parts[0]);
   size_t offs[kParts], total = 0;
   for (int i = 0; i < kParts; ++i) {
@@ -90,6 +91,8 @@ sta_status device_tables(const sta_plan *p, void *stream, DeviceTables *out) {
   t.ptab = p->ptab.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[13]);
   t.gtab = p->gtab.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[14]);
   t.queue = p->queue.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[15]);
+  t.wlist = p->woff.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[16]);
+  t.woff = p->woff.empty() ? nullptr : reinterpret_cast<int32_t *>(b + offs[17]);
   t.block = block;
   t.upload_stream = stream;
   t.ready = ready;
@@ -306,7 +309,7 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
     st = forward_scratch(p, stream, &scratch);
     if (st != STA_OK) return st;
   }
-  sta::FwdArgs a;
+  sta::FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = out;
   a.sched = t.sched;
   a.kv_off = t.kv_off;
@@ -339,6 +342,9 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   if (p->dyn_blocks) a.n_blocks = p->dyn_blocks;
   a.ptab = t.ptab;
   a.gtab = t.gtab;
+  a.wlist = t.wlist;
+  a.woff = t.woff;
+  if (!p->woff.empty()) a.n_blocks = (int32_t)p->woff.size() - 1;
   a.pcount = a.qcount + kQueueWords;
   a.fbits = reinterpret_cast<unsigned *>(a.pcount + p->n_groups);
   a.flist = a.qcount + fwd_zero_words(p->n_groups, p->items());

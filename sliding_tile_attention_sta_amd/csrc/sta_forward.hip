@@ -94,7 +94,7 @@ __device__ __forceinline__ int tok_start(int x, int w, int e) {
 
 // D: head dim.  QB: 16-query blocks per wave.  NW: waves per group.
 template <int D, int QB, int NW, bool F32IN, bool F32OUT, bool PARTIAL, bool SWA = false, bool SEP = false,
-          bool FIXUP = false>
+          bool FIXUP = false, bool MULTI = false>
 __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int QPI = 16 * QB * NW;               // queries per work item
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
   __shared__ int last_piece;      // a split item's piece: the last one to arrive
   __shared__ unsigned vmax_bits;  // FIXUP: largest |v| of the item's keys
   int item = -1;
-  if constexpr (FIXUP) {
+  if constexpr (FIXUP || MULTI) {
   } else if (a.queue != nullptr) {
     __shared__ int taken;
     if (tid == 0) {
@@ -164,9 +164,18 @@ __global__ __launch_bounds__(NW * 64) void sta_fwd_kernel(FwdArgs a) {
       for (int i = 0; i < 11; ++i) __hip_atomic_store(a.qcount + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
-  if (!FIXUP && item == -1) {
+  if (!FIXUP && !MULTI && item == -1) {
     finish();
     return;
+  }
+  // MULTI (plans with fewer work items than compute units): work group b
+  // runs the entries wlist[woff[b] .. woff[b+1]) in turn, whole items and
+  // pieces of one contiguous range of the launch's key steps, so that every
+  // compute unit walks the same number of steps.
+  int w_k = 0, w_end = 0;
+  if constexpr (MULTI) {
+    w_k = __builtin_amdgcn_readfirstlane(a.woff[blockIdx.x]);
+    w_end = __builtin_amdgcn_readfirstlane(a.woff[blockIdx.x + 1]);
   }
   // FIXUP: the items the forward marked (V beyond fp16's range, see the
   // check after the walk), taken in turn by the work groups and redone with
@@ -190,6 +199,10 @@ next_item:
     }
     item = __builtin_amdgcn_readfirstlane(a.flist[fix_k]);
     fix_k += gridDim.x;
+  } else if constexpr (MULTI) {
+    if (w_k >= w_end) return;
+    item = __builtin_amdgcn_readfirstlane(a.wlist[w_k]);
+    ++w_k;
   }
   int piece = -1, s_first = 0, s_end = 0;
   if (item < -1) {
@@ -722,7 +735,9 @@ next_item:
 
   // ---- a piece of a split item: publish the partial result (unnormalised
   // O, reference maxima and row-sum partials); the group's last piece to
-  // arrive combines all of them and finalizes.  Softmax pieces combine
+  // arrive combines all of them and finalizes (with per-work-group lists, a
+  // piece that starts its publication after every other one has arrived
+  // skips it).  Softmax pieces combine
   // exactly: with M = max of the pieces' reference maxima (exp2 units),
   // O = sum_p 2^(mb_p - M) O_p and l = sum_p 2^(mb_p - M) l_p.  Pieces may
   // run on different XCDs, whose L2 caches are not coherent with each
@@ -741,63 +756,147 @@ next_item:
           for (int j = 0; j < QB; ++j) o[b][j] *= oscale;
         oscale = 1.f;
       }
-      constexpr int SLOT = 384 * D + 2 * QB * NT;   // floats per slot (fwd_slot_floats)
-      constexpr int ML = DB * QB * NT * 4;           // float offset of the maxima and row sums
-      {
-        float *slot = a.pslot + (size_t)piece * SLOT;
+      if constexpr (MULTI) {
+        // Per-work-group lists: a piece that finds every other one of its
+        // group arrived skips its publication.  Kept apart from the section
+        // below, which the large launches run: there the same source with a
+        // run-time branch cost 1 % through code layout.
+        constexpr int SLOT = 384 * D + 2 * QB * NT;   // floats per slot (fwd_slot_floats)
+        constexpr int ML = DB * QB * NT * 4;           // float offset of the maxima and row sums
+        const int group = __builtin_amdgcn_readfirstlane(a.ptab[4 * piece + 3]);
+        const int first = __builtin_amdgcn_readfirstlane(a.gtab[2 * group]);
+        const int np = __builtin_amdgcn_readfirstlane(a.gtab[2 * group + 1]);
+        // A piece that finds every other piece of its group arrived is the
+        // last: it publishes nothing and keeps its own partial in registers
+        // (acquire: the relaxed load that saw the count, then a fence).
+        if (tid == 0) {
+          const bool all =
+              __hip_atomic_load(a.pcount + group, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+          if (all) {
+            __threadfence();                                 // acquire
+            atomicExch(a.pcount + group, 0);                 // ready for the next launch
+          }
+          last_piece = all ? 2 : 0;
+        }
+        __syncthreads();
+        if (last_piece == 0) {
+          float *slot = a.pslot + (size_t)piece * SLOT;
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+          for (int b = 0; b < DB; ++b)
 #pragma unroll
-          for (int j = 0; j < QB; ++j) reinterpret_cast<f32x4 *>(slot)[(b * QB + j) * NT + tid] = o[b][j];
+            for (int j = 0; j < QB; ++j) reinterpret_cast<f32x4 *>(slot)[(b * QB + j) * NT + tid] = o[b][j];
+#pragma unroll
+          for (int j = 0; j < QB; ++j) {
+            slot[ML + j * NT + tid] = mb[j];
+            slot[ML + (QB + j) * NT + tid] = l[j];
+          }
+          // Every wave's stores have reached its XCD's L2 before the release.
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (tid == 0) {
+            __threadfence();                                 // release
+            const bool last = atomicAdd(a.pcount + group, 1) == np - 1;
+            if (last) {
+              __threadfence();                               // acquire
+              atomicExch(a.pcount + group, 0);               // ready for the next launch
+            }
+            last_piece = last;
+          }
+          __syncthreads();
+          if (!last_piece) {
+            __syncthreads();
+            goto next_item;
+          }
+        }
+        // Combined in piece order as below, the own partial taken from
+        // registers (the same values as its published copy).
 #pragma unroll
         for (int j = 0; j < QB; ++j) {
-          slot[ML + j * NT + tid] = mb[j];
-          slot[ML + (QB + j) * NT + tid] = l[j];
+          float mx = -INFINITY;
+          for (int p = first; p < first + np; ++p)
+            mx = fmaxf(mx, p == piece ? mb[j] : a.pslot[(size_t)p * SLOT + ML + j * NT + tid]);
+          float lj = 0.f;
+          f32x4 oj[DB];
+#pragma unroll
+          for (int b = 0; b < DB; ++b) oj[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int p = first; p < first + np; ++p) {
+            if (p == piece) {
+              const float f = __builtin_amdgcn_exp2f(mb[j] - mx);
+              lj += f * l[j];
+#pragma unroll
+              for (int b = 0; b < DB; ++b) oj[b] += f * o[b][j];
+            } else {
+              const float *slot = a.pslot + (size_t)p * SLOT;
+              const float f = __builtin_amdgcn_exp2f(slot[ML + j * NT + tid] - mx);
+              lj += f * slot[ML + (QB + j) * NT + tid];
+#pragma unroll
+              for (int b = 0; b < DB; ++b) oj[b] += f * reinterpret_cast<const f32x4 *>(slot)[(b * QB + j) * NT + tid];
+            }
+          }
+          mb[j] = mx;
+          l[j] = lj;
+#pragma unroll
+          for (int b = 0; b < DB; ++b) o[b][j] = oj[b];
         }
-      }
-      // Every wave's stores have reached its XCD's L2 before the release.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      const int group = __builtin_amdgcn_readfirstlane(a.ptab[4 * piece + 3]);
-      const int first = __builtin_amdgcn_readfirstlane(a.gtab[2 * group]);
-      const int np = __builtin_amdgcn_readfirstlane(a.gtab[2 * group + 1]);
-      if (tid == 0) {
-        __threadfence();                                   // release
-        const bool last = atomicAdd(a.pcount + group, 1) == np - 1;
-        if (last) {
-          __threadfence();                                 // acquire
-          atomicExch(a.pcount + group, 0);                 // ready for the next launch
+      } else {
+        constexpr int SLOT = 384 * D + 2 * QB * NT;   // floats per slot (fwd_slot_floats)
+        constexpr int ML = DB * QB * NT * 4;           // float offset of the maxima and row sums
+        {
+          float *slot = a.pslot + (size_t)piece * SLOT;
+#pragma unroll
+          for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int j = 0; j < QB; ++j) reinterpret_cast<f32x4 *>(slot)[(b * QB + j) * NT + tid] = o[b][j];
+#pragma unroll
+          for (int j = 0; j < QB; ++j) {
+            slot[ML + j * NT + tid] = mb[j];
+            slot[ML + (QB + j) * NT + tid] = l[j];
+          }
         }
-        last_piece = last;
-      }
-      __syncthreads();
-      if (!last_piece) {
-        finish();
-        return;
-      }
-      // Combined in piece order, every partial read back (the last piece's
-      // own included), so that the result does not depend on which piece
-      // arrived last; one query block at a time, which keeps the loads of
-      // one partial block beside the accumulators in registers.
-#pragma unroll
-      for (int j = 0; j < QB; ++j) {
-        float mx = -INFINITY;
-        for (int p = first; p < first + np; ++p) mx = fmaxf(mx, a.pslot[(size_t)p * SLOT + ML + j * NT + tid]);
-        float lj = 0.f;
-        f32x4 oj[DB];
-#pragma unroll
-        for (int b = 0; b < DB; ++b) oj[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int p = first; p < first + np; ++p) {
-          const float *slot = a.pslot + (size_t)p * SLOT;
-          const float f = __builtin_amdgcn_exp2f(slot[ML + j * NT + tid] - mx);
-          lj += f * slot[ML + (QB + j) * NT + tid];
-#pragma unroll
-          for (int b = 0; b < DB; ++b) oj[b] += f * reinterpret_cast<const f32x4 *>(slot)[(b * QB + j) * NT + tid];
+        // Every wave's stores have reached its XCD's L2 before the release.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const int group = __builtin_amdgcn_readfirstlane(a.ptab[4 * piece + 3]);
+        const int first = __builtin_amdgcn_readfirstlane(a.gtab[2 * group]);
+        const int np = __builtin_amdgcn_readfirstlane(a.gtab[2 * group + 1]);
+        if (tid == 0) {
+          __threadfence();                                   // release
+          const bool last = atomicAdd(a.pcount + group, 1) == np - 1;
+          if (last) {
+            __threadfence();                                 // acquire
+            atomicExch(a.pcount + group, 0);                 // ready for the next launch
+          }
+          last_piece = last;
         }
-        mb[j] = mx;
-        l[j] = lj;
+        __syncthreads();
+        if (!last_piece) {
+          finish();
+          return;
+        }
+        // Combined in piece order, every partial read back (the last piece's
+        // own included), so that the result does not depend on which piece
+        // arrived last; one query block at a time, which keeps the loads of
+        // one partial block beside the accumulators in registers.
 #pragma unroll
-        for (int b = 0; b < DB; ++b) o[b][j] = oj[b];
+        for (int j = 0; j < QB; ++j) {
+          float mx = -INFINITY;
+          for (int p = first; p < first + np; ++p) mx = fmaxf(mx, a.pslot[(size_t)p * SLOT + ML + j * NT + tid]);
+          float lj = 0.f;
+          f32x4 oj[DB];
+#pragma unroll
+          for (int b = 0; b < DB; ++b) oj[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int p = first; p < first + np; ++p) {
+            const float *slot = a.pslot + (size_t)p * SLOT;
+            const float f = __builtin_amdgcn_exp2f(slot[ML + j * NT + tid] - mx);
+            lj += f * slot[ML + (QB + j) * NT + tid];
+#pragma unroll
+            for (int b = 0; b < DB; ++b) oj[b] += f * reinterpret_cast<const f32x4 *>(slot)[(b * QB + j) * NT + tid];
+          }
+          mb[j] = mx;
+          l[j] = lj;
+#pragma unroll
+          for (int b = 0; b < DB; ++b) o[b][j] = oj[b];
+        }
       }
     }
   }
@@ -830,7 +929,7 @@ next_item:
       }
     }
   }
-  if constexpr (FIXUP) {
+  if constexpr (FIXUP || MULTI) {
     __syncthreads();
     goto next_item;
   } else {
@@ -843,9 +942,10 @@ __global__ void zero_kernel(int32_t *p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
-template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL, bool SWA, bool SEP, bool FIXUP>
+template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL, bool SWA, bool SEP, bool FIXUP,
+          bool MULTI = false>
 hipError_t launch_kernel(const FwdArgs &a, int blocks, hipStream_t s) {
-  auto kern = sta_fwd_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, SEP, FIXUP>;
+  auto kern = sta_fwd_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, SEP, FIXUP, MULTI>;
   const size_t lds = (size_t)fwd_lds_bytes(D, a.V, a.max_nkv) +
                      (PARTIAL || SEP ? (size_t)fwd_lds_step_bytes(a.V, a.max_nkv) : 0);
   if (lds > kMaxLds) return hipErrorInvalidValue;
@@ -864,7 +964,13 @@ hipError_t launch_kernel(const FwdArgs &a, int blocks, hipStream_t s) {
 // and V through the tile tables (SEP off): it is the rare path.
 template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL, bool SWA = false, bool SEP = false>
 hipError_t launch_one(const FwdArgs &a, hipStream_t s) {
-  hipError_t e = launch_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, SEP, false>(a, a.n_blocks, s);
+  hipError_t e;
+  if constexpr (!SWA && QB == 3 && NW == 8) {
+    e = a.wlist != nullptr ? launch_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, SEP, false, true>(a, a.n_blocks, s)
+                           : launch_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, SEP, false>(a, a.n_blocks, s);
+  } else {
+    e = launch_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, SEP, false>(a, a.n_blocks, s);
+  }
   if (e != hipSuccess) return e;
   return launch_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, false, true>(a, 256, s);
 }
@@ -902,8 +1008,10 @@ hipError_t launch_zero(int32_t *p, int n, hipStream_t stream) {
 hipError_t launch_forward(const FwdArgs &a, int variant, int head_dim, bool f32_in, bool f32_out,
                           hipStream_t stream) {
   if (a.n_blocks <= 0) return hipSuccess;
-  // Split items exist only for the 384-query kernel (not token-wise SWA).
-  if (a.ptab != nullptr && (variant != kTile384 || a.swin != nullptr)) return hipErrorInvalidValue;
+  // Split items and per-group lists exist only for the 384-query kernel
+  // (not token-wise SWA).
+  if ((a.ptab != nullptr || a.wlist != nullptr) && (variant != kTile384 || a.swin != nullptr))
+    return hipErrorInvalidValue;
   if (variant == kTile384) {
     if (head_dim == 128) return launch_p<128, 3, 8>(a, f32_in, f32_out, stream);
     return launch_p<64, 3, 8>(a, f32_in, f32_out, stream);

@@ -76,6 +76,8 @@ struct DeviceTables {
   int32_t *queue = nullptr;        // dynamic queues: the 8 XCD queues, concatenated
   int32_t *ptab = nullptr;         // split items: 4 per piece (item, first step, end step, group)
   int32_t *gtab = nullptr;         // split items: 2 per group (first piece, piece count)
+  int32_t *wlist = nullptr;        // per-work-group lists (codes), and
+  int32_t *woff = nullptr;         // their offsets (launch blocks + 1)
   void *block = nullptr;           // the single allocation holding all of the above
   // The upload runs on the stream of the call that made it; `ready` (a
   // hipEvent_t) is recorded after it, and a call on another stream waits
@@ -151,6 +153,12 @@ struct sta_plan {
   std::vector<int32_t> queue;
   int32_t qoff[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   int32_t dyn_blocks = 0;
+  // Plans with fewer work items than compute units: the launch's key steps
+  // (all items in decreasing-cost order, concatenated) are cut into one
+  // contiguous range per compute unit; work group b runs the whole items
+  // and pieces of its range, the codes wlist[woff[b] .. woff[b+1]), in
+  // turn.  Empty otherwise.
+  std::vector<int32_t> wlist, woff;
   std::vector<int32_t> base_nat, off_nat;
   std::vector<int32_t> base_tm, off_tm;   // tile-major layout: tile * V, identity
   int64_t pairs = 0;

@@ -47,6 +47,10 @@ struct FwdArgs {
   const int32_t *gtab;
   int32_t *pcount;
   float *pslot;
+  // Per-work-group lists (NULL otherwise): work group b runs the codes
+  // wlist[woff[b] .. woff[b+1]) in turn (whole items and pieces).
+  const int32_t *wlist;
+  const int32_t *woff;
   int32_t n_items, n_pieces;   // item codes in [0, n_items), pieces in [0, n_pieces)
   unsigned *dbg;               // debug builds: bounds-check violation bits (else unused)
 };

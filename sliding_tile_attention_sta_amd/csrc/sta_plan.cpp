@@ -96,12 +96,18 @@ constexpr int64_t kMinPieceSteps = 32;
 // steps), R = 64 (a quarter of the chip's compute units), k = 4, fewer if a
 // piece would walk less than 32 steps or there would be more than 512
 // pieces, and no split at k < 2.  With fewer items than compute units,
-// every item, into the k whose pieces take the fewest rounds of the chip
-// (12x24x24's 144 items: k = 3, two rounds of a third of an item).
+// either one contiguous range of key steps per compute unit (per-work-group
+// lists, sta_plan::wlist, where that pays by more than kRangeOverheadSteps)
+// or every item into the k whose pieces take the fewest rounds of the chip.
 // Measured on MI355X with the 7,200 equal items of the 720p workload: 64
 // items in 4 pieces ran 1 % faster than no split; 128 or 256 items in 4
 // pieces less so, and 256 in 8 slower than no split (every piece adds the
 // write of its partial result, two fences and its share of the merge).
+//
+// A range pays only if it saves more than this many 32-key steps against
+// one round of whole items (measured on MI355X: see build_forward_queues).
+constexpr int64_t kRangeOverheadSteps = 32;
+
 template <typename Off>
 void build_forward_queues(sta_plan *p, const std::vector<Off> &off, int64_t steps_per_entry, int64_t align,
                           bool split) {
@@ -114,6 +120,72 @@ void build_forward_queues(sta_plan *p, const std::vector<Off> &off, int64_t step
     return ((int64_t)off[(size_t)h * p->n_tiles + t + 1] - off[(size_t)h * p->n_tiles + t]) * steps_per_entry;
   };
   const int64_t units = kXcds * kCusPerXcd;
+  int64_t total_steps = 0, max_steps = 0;
+  for (int64_t i = 0; i < n_items; ++i) {
+    total_steps += steps(order[i]);
+    max_steps = std::max(max_steps, steps(order[i]));
+  }
+  if (split && n_items > 0 && n_items < units && total_steps + kRangeOverheadSteps * units < max_steps * units) {
+    // Fewer items than compute units, and one range of the launch's key
+    // steps per compute unit beats one round of whole items by more than a
+    // range's overhead (its pieces' publication and merge, and a second
+    // item's prologue): the ranges are contiguous (boundaries on multiples
+    // of align steps), so every unit walks the same number of steps (within
+    // align).  12x24x24's 144 items of 216 steps: 121.5 steps per unit
+    // against two rounds of 72-step pieces; one round of 192 items of 108
+    // steps stays whole (81 steps per range ran 5 % slower on MI355X).  An
+    // item inside one range runs whole; an item cut by range boundaries
+    // becomes a group of pieces that merge as in the tail split.  Ranges 32
+    // apart go to the same XCD (range u to block (u mod 32) * 8 + u / 32,
+    // blocks being dispatched to XCDs round-robin), so ranges that share an
+    // item share an L2.
+    std::vector<int64_t> start(n_items + 1, 0);
+    for (int64_t i = 0; i < n_items; ++i) start[i + 1] = start[i] + steps(order[i]) / align;
+    const int64_t total = start[n_items];
+    std::vector<std::vector<std::pair<int64_t, int64_t>>> cut(n_items);   // (lo, hi) per item
+    std::vector<std::vector<std::pair<int64_t, int64_t>>> unit_of(n_items);   // (unit, piece slot)
+    int64_t it = 0;
+    for (int64_t u = 0; u < units; ++u) {
+      int64_t lo = total * u / units;
+      const int64_t hi = total * (u + 1) / units;
+      while (lo < hi) {
+        while (start[it + 1] <= lo) ++it;
+        const int64_t e = std::min(hi, start[it + 1]);
+        unit_of[it].push_back({u, (int64_t)cut[it].size()});
+        cut[it].push_back({lo - start[it], e - start[it]});
+        lo = e;
+      }
+    }
+    std::vector<std::vector<int32_t>> codes(units);
+    for (int64_t i = 0; i < n_items; ++i) {
+      if (cut[i].size() == 1) {
+        codes[unit_of[i][0].first].push_back((int32_t)order[i]);
+        continue;
+      }
+      const int32_t group = p->n_groups++;
+      p->gtab.push_back(p->n_pieces);
+      p->gtab.push_back((int32_t)cut[i].size());
+      for (size_t j = 0; j < cut[i].size(); ++j) {
+        p->ptab.push_back((int32_t)order[i]);
+        p->ptab.push_back((int32_t)(cut[i][j].first * align));
+        p->ptab.push_back((int32_t)(cut[i][j].second * align));
+        p->ptab.push_back(group);
+        codes[unit_of[i][j].first].push_back(-2 - p->n_pieces++);
+      }
+    }
+    p->woff.assign(units + 1, 0);
+    p->wlist.clear();
+    for (int64_t b = 0; b < units; ++b) {
+      const int64_t u = (b % kXcds) * kCusPerXcd + b / kXcds;
+      p->wlist.insert(p->wlist.end(), codes[u].begin(), codes[u].end());
+      p->woff[b + 1] = (int32_t)p->wlist.size();
+    }
+    p->sched = p->wlist;
+    p->queue.clear();
+    for (int x = 0; x < 10; ++x) p->qoff[x] = 0;
+    p->dyn_blocks = 0;
+    return;
+  }
   int64_t best_r = 0;
   int best_k = 1;
   if (split && n_items > 0) {
@@ -573,7 +645,9 @@ sta_status sta_plan_get_info(const sta_plan *p, sta_plan_info *info) {
   info->split_items = p->n_groups;
   info->pieces = p->n_pieces;
   info->scratch_bytes = p->fwd_scratch();
-  info->launch_blocks = p->dyn_blocks ? p->dyn_blocks : (int64_t)p->sched.size();
+  info->launch_blocks = p->dyn_blocks ? p->dyn_blocks
+                        : !p->woff.empty() ? (int64_t)p->woff.size() - 1
+                                           : (int64_t)p->sched.size();
   return STA_OK;
 }
 
@@ -646,6 +720,14 @@ sta_status sta_plan_schedule(const sta_plan *p, int32_t *out, int64_t cap, int64
   *count = (int64_t)p->sched.size();
   if (cap < *count || !out) return STA_ERR_ARG;
   std::memcpy(out, p->sched.data(), p->sched.size() * sizeof(int32_t));
+  return STA_OK;
+}
+
+sta_status sta_plan_group_lists(const sta_plan *p, int32_t *out, int64_t cap, int64_t *count) {
+  if (!p || !count) return STA_ERR_ARG;
+  *count = (int64_t)p->woff.size();
+  if (cap < *count || (!out && *count > 0)) return STA_ERR_ARG;
+  if (*count > 0) std::memcpy(out, p->woff.data(), p->woff.size() * sizeof(int32_t));
   return STA_OK;
 }
 

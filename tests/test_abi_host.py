@@ -96,6 +96,9 @@ def test_schedule_covers_every_item_once_and_balances_xcds(name):
     info = p.info
     subs = info.tile_tokens // info.queries_per_item
     n_items = w.batch * w.heads * info.n_tiles * subs
+    if len(p.group_lists()):
+        _check_group_lists(w, p, partial)
+        return
     # the XCD queues interleaved (entry s * 8 + x of XCD x's queue, -1
     # padding), then the pieces of split items in the order they are taken
     n_whole = len(s) - info.pieces
@@ -149,6 +152,81 @@ def test_schedule_covers_every_item_once_and_balances_xcds(name):
         assert info.launch_blocks >= len(s)
     else:
         assert info.launch_blocks == len(s)
+
+
+def _check_group_lists(w, p, partial):
+    """Per-work-group lists: work group b runs range u = (b mod 8) * 32 +
+    b // 8 of the launch's key steps; the ranges, in order, walk the items
+    in decreasing-cost order, each item's steps in order, and every range
+    holds the same number of steps (within one alignment unit)."""
+    info = p.info
+    s, off = p.schedule().numpy(), p.group_lists().numpy()
+    subs = info.tile_tokens // info.queries_per_item
+    n_items = w.batch * w.heads * info.n_tiles * subs
+    assert info.launch_blocks == 256 and len(off) == 257
+    assert off[0] == 0 and off[-1] == len(s) and (np.diff(off) >= 0).all()
+    assert (s != -1).all()
+    pieces = p.pieces().numpy()
+    assert sorted((-2 - s[s < -1]).tolist()) == list(range(info.pieces))
+    grid = O.tile_grid(w.video, w.tile, partial)
+    spt = info.tile_tokens // 32
+    align = spt if partial else 1
+
+    def steps_of(code):
+        h = (code // subs // info.n_tiles) % w.heads
+        we = O.effective_window(w.windows[h], grid)
+        return we[0] * we[1] * we[2] * spt
+
+    walk = []   # (item, first step, end step) per range entry, in range order
+    per_unit = []
+    for u in range(256):
+        b = (u % 32) * 8 + u // 32
+        n = 0
+        for code in s[off[b]:off[b + 1]].tolist():
+            if code >= 0:
+                walk.append((code, 0, steps_of(code)))
+            else:
+                it, a, e, g, npc = pieces[-2 - code].tolist()
+                walk.append((it, a, e))
+            n += walk[-1][2] - walk[-1][1]
+        per_unit.append(n)
+    total = sum(per_unit)
+    assert total == sum(steps_of(c) for c in range(n_items))
+    assert max(per_unit) - min(per_unit) <= align
+    items = []
+    for (it, a, e), nxt in zip(walk, walk[1:] + [None]):
+        assert a < e and a % align == 0
+        if not items or items[-1][0] != it:
+            assert a == 0
+            items.append([it, e])
+        else:
+            assert a == items[-1][1]
+            items[-1][1] = e
+    assert sorted(it for it, _ in items) == list(range(n_items))
+    assert all(e == steps_of(it) for it, e in items)
+    costs = [steps_of(it) for it, _ in items]
+    assert costs == sorted(costs, reverse=True)
+    # pieces record their group's size
+    for it, a, e, g, npc in pieces.tolist():
+        assert npc == sum(1 for x in pieces.tolist() if x[3] == g)
+
+
+def test_group_lists_only_where_they_pay():
+    """Per-work-group ranges replace whole items only where the balanced
+    range beats one round of the costliest item by the range overhead
+    (32 steps): 12x24x24 (144 items of 216 steps: 121.5 per range) takes
+    them; 2d (192 items of 108 steps: 81 per range) and every launch with
+    at least 256 items do not."""
+    for name, lists in (("small", True), ("2d", False), ("720p", False), ("tiny", False)):
+        w = WORKLOADS[name]
+        i = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+        assert (len(i.group_lists()) > 0) == lists, name
+    lib = L.lib()
+    n = ctypes.c_int64()
+    assert lib.sta_plan_group_lists(None, None, 0, ctypes.byref(n)) == L.STA_ERR_ARG
+    w = WORKLOADS["small"]
+    p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    assert lib.sta_plan_group_lists(p.handle, None, 0, ctypes.byref(n)) == L.STA_ERR_ARG and n.value == 257
 
 
 def test_tail_is_split_only_where_it_pays():
