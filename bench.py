@@ -132,13 +132,19 @@ def cpu_baseline(w, q, k, v, budget_s=12.0):
                 break
         h += 1
     full_s = t_used * O.sta_flops(w.video, w.tile, w.windows, w.head_dim, w.batch) / flops
+    if done_tiles == w.heads * sum(1 for _ in sample_query_tiles(w, 0)) and \
+            all(len(list(sample_query_tiles(w, x))) == grid[0] * grid[1] * grid[2] for x in range(w.heads)):
+        sample = (f"every query tile of every head of the {w.name} workload ({done_tiles}: the whole "
+                  f"call), float64 numpy, {t_used:.2f} s")
+    else:
+        sample = (f"{done_tiles} query tiles (heads 0..{h - 1}) of the {w.name} workload, "
+                  f"float64 numpy, {t_used:.1f} s; a full call extrapolates to {full_s:.0f} s")
     return {
         "value": flops / t_used / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{done_tiles} query tiles (heads 0..{h - 1}) of the {w.name} workload, "
-                  f"float64 numpy, {t_used:.1f} s; a full call extrapolates to {full_s:.0f} s",
+        "sample": sample,
         "seconds": t_used,
         "cpu_model": _cpu_model(),
     }
