@@ -211,6 +211,17 @@ def _check_group_lists(w, p, partial):
         assert npc == sum(1 for x in pieces.tolist() if x[3] == g)
 
 
+def test_group_lists_with_partial_tiles_break_on_key_tiles():
+    """12x22x24 with 6x8x8 tiles (the last H row partial): the per-unit
+    ranges are whole key tiles, so every piece starts on a key tile's first
+    (always existing) token."""
+    from sliding_tile_attention_sta_amd.synthetic import Workload
+    w = Workload("small-partial", 21, (12, 22, 24), (6, 8, 8), ((3, 3, 3),) * 8, 128, "bf16")
+    p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim, partial_tiles=True)
+    assert len(p.group_lists()) == 257 and p.info.partial_tiles == 1
+    _check_group_lists(w, p, True)
+
+
 def test_group_lists_only_where_they_pay():
     """Per-work-group ranges replace whole items only where the balanced
     range beats one round of the costliest item by the range overhead

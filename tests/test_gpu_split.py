@@ -8,7 +8,9 @@ include/sta.h).  Checked here, against the float64 oracle on the very same
 inputs: every query tile of every split item (output within the forward's
 parity bound, row log-sum-exp within 1e-3), on the workloads whose plans
 split (720p, 60x48x80, 12x24x24 where every item is split, and 30x45x80
-with partial tiles, whose pieces start on key-tile boundaries); that two launches give the same bits (the merge does not
+and 12x22x24 with partial tiles, whose pieces start on key-tile
+boundaries; the 12x... workloads run one range of key steps per compute
+unit); that two launches give the same bits (the merge does not
 depend on which piece arrives last, nor the result on which work group
 takes which queue entry, and every launch leaves the queue words and
 arrival counters ready for the next one), also after a launch on other
@@ -24,7 +26,7 @@ import torch
 from oracle import sta_oracle as O
 from oracle import sta_oracle_bwd as OB
 from sliding_tile_attention_sta_amd import api
-from sliding_tile_attention_sta_amd.synthetic import WORKLOADS, make_qkv
+from sliding_tile_attention_sta_amd.synthetic import WORKLOADS, Workload, make_qkv
 
 MAX_ABS, MEAN_ABS, LSE_ABS = 2e-2, 2e-3, 1e-3
 
@@ -56,9 +58,15 @@ def window_rows(x, w, c, b, h, grid):
     return np.asarray(s, np.float64).reshape(-1, x.shape[-1])
 
 
-@pytest.mark.parametrize("name", ["720p", "long", "small", "720p-exact"])
+# 12x22x24 with 6x8x8 tiles: the last tile row along H is partial, and its
+# 144 items take one range of key steps per compute unit, cut on key-tile
+# boundaries (a piece's first key block must hold an existing key).
+SMALL_PARTIAL = Workload("small-partial", 21, (12, 22, 24), (6, 8, 8), ((3, 3, 3),) * 8, 128, "bf16")
+
+
+@pytest.mark.parametrize("name", ["720p", "long", "small", "720p-exact", "small-partial"])
 def test_split_items_match_oracle(name):
-    w = WORKLOADS[name]
+    w = SMALL_PARTIAL if name == "small-partial" else WORKLOADS[name]
     partial = any(e % t for e, t in zip(w.video, w.tile))
     say(f"case split {name}")
     plan = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim, partial_tiles=partial)
