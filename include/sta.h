@@ -75,7 +75,8 @@ typedef struct {
   int64_t tokens;           /* T*H*W */
   int64_t pairs;            /* attended (query tile, key tile) pairs, summed over heads, one batch element */
   double flops;             /* 4 * tile_tokens^2 * head_dim * pairs * batch: FLOPs of the two products */
-  int64_t work_items;       /* launched work items (including idle padding items) */
+  int64_t work_items;       /* entries of the forward schedule (sta_plan_schedule): work items,
+                               idle padding and pieces */
   int32_t queries_per_item; /* query tokens per work item */
   int32_t kernel_variant;   /* 0 = generic (32 queries / item), 1 = 384-query items */
   int32_t bwd_supported;    /* 1 if sta_backward_plan accepts this plan */
@@ -89,7 +90,8 @@ typedef struct {
   int32_t pieces;           /* launched pieces of those items */
   int64_t scratch_bytes;    /* device scratch a forward launch of this plan uses (queue and
                                arrival counters, fix-up marks, partial results of pieces) */
-  int64_t launch_blocks;    /* work groups of one forward launch */
+  int64_t launch_blocks;    /* work groups of one forward launch (256 with per-work-group
+                               lists, see sta_plan_group_lists) */
 } sta_plan_info;
 
 /* Source: "Fast Video Generation with Sliding Tile Attention", index page,
