@@ -107,6 +107,11 @@ constexpr int64_t kMinPieceSteps = 32;
 // A range pays only if it saves more than this many 32-key steps against
 // one round of whole items (measured on MI355X: see build_forward_queues).
 constexpr int64_t kRangeOverheadSteps = 32;
+// Per-unit ranges need at least units / this many items.  12x24x24 with one
+// head (18 items, about 15 ranges each) ran 3.5 % slower in ranges than in
+// the 4-way split below; with two heads (36 items, about 7 ranges each)
+// 2.6 % faster (MI355X, one session).
+constexpr int64_t kMaxRangesPerItem = 8;
 
 template <typename Off>
 void build_forward_queues(sta_plan *p, const std::vector<Off> &off, int64_t steps_per_entry, int64_t align,
@@ -125,9 +130,12 @@ void build_forward_queues(sta_plan *p, const std::vector<Off> &off, int64_t step
     total_steps += steps(order[i]);
     max_steps = std::max(max_steps, steps(order[i]));
   }
-  if (split && n_items > 0 && n_items < units && total_steps + kRangeOverheadSteps * units < max_steps * units) {
-    // Fewer items than compute units, and one range of the launch's key
-    // steps per compute unit beats one round of whole items by more than a
+  if (split && n_items * kMaxRangesPerItem >= units && n_items < units &&
+      total_steps + kRangeOverheadSteps * units < max_steps * units) {
+    // Fewer items than compute units (but not so few that an item spans
+    // more than about kMaxRangesPerItem ranges, whose partial results its
+    // last piece would read back), and one range of the launch's key steps
+    // per compute unit beats one round of whole items by more than a
     // range's overhead (its pieces' publication and merge, and a second
     // item's prologue): the ranges are contiguous (boundaries on multiples
     // of align steps), so every unit walks the same number of steps (within

@@ -225,13 +225,18 @@ def test_group_lists_with_partial_tiles_break_on_key_tiles():
 def test_group_lists_only_where_they_pay():
     """Per-work-group ranges replace whole items only where the balanced
     range beats one round of the costliest item by the range overhead
-    (32 steps): 12x24x24 (144 items of 216 steps: 121.5 per range) takes
-    them; 2d (192 items of 108 steps: 81 per range) and every launch with
-    at least 256 items do not."""
-    for name, lists in (("small", True), ("2d", False), ("720p", False), ("tiny", False)):
-        w = WORKLOADS[name]
+    (32 steps) and no item spans more than about 8 ranges: 12x24x24 with 8
+    or 2 heads (144 or 36 items of 216 steps) takes them; with 1 head (18
+    items, about 15 ranges each) it keeps the 4-way split; 2d (192 items of
+    108 steps: 81 per range) and every launch with at least 256 items do
+    not."""
+    for name, heads, lists in (("small", 8, True), ("small", 2, True), ("small", 1, False), ("2d", 8, False),
+                               ("720p", 24, False), ("tiny", 2, False)):
+        w = WORKLOADS[name].with_heads(heads)
         i = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
-        assert (len(i.group_lists()) > 0) == lists, name
+        assert (len(i.group_lists()) > 0) == lists, (name, heads)
+        if name == "small" and not lists:
+            assert i.info.pieces == 4 * 18   # one round of the 4-way split instead
     lib = L.lib()
     n = ctypes.c_int64()
     assert lib.sta_plan_group_lists(None, None, 0, ctypes.byref(n)) == L.STA_ERR_ARG
