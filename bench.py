@@ -33,8 +33,11 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed calls (default 50; 3 for the window search, whose sweep takes seconds)")
-    ap.add_argument("--warmup", type=int, default=None, help="untimed calls first (default 10; 1 for search)")
+                    help="timed calls (default 50, more for calls under 5 ms: at least 0.25 s of them; "
+                         "3 for the window search, whose sweep takes seconds)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed calls first (default 10, more for calls under 10 ms: at least 0.1 s "
+                         "of them, so that the clock has settled; 1 for search)")
     ap.add_argument("--workload", default="720p")
     ap.add_argument("--pass", dest="which", choices=["forward", "backward", "search", "swa"],
                     default="forward",
@@ -51,11 +54,35 @@ def parse():
                                                            "profiles", "traffic.json"))
     args = ap.parse_args()
     search = args.which == "search"
+    args.auto_steps, args.auto_warmup = args.steps is None, args.warmup is None
     if args.steps is None:
         args.steps = 3 if search else 50
     if args.warmup is None:
         args.warmup = 1 if search else 10
     return args
+
+
+def fit_counts(args, fn, stream):
+    """Default call counts for short calls: warm up for at least 0.1 s and
+    time at least 0.25 s of calls (10 and 50 at least; flags given on the
+    command line are kept)."""
+    import math
+    import torch
+    if not (args.auto_steps or args.auto_warmup):
+        return
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = max(e0.elapsed_time(e1), 1e-3)
+    if args.auto_warmup:
+        args.warmup = min(20000, max(args.warmup, math.ceil(100.0 / ms)))
+    if args.auto_steps:
+        args.steps = min(20000, max(args.steps, math.ceil(250.0 / ms)))
 
 
 def timed(fn, steps, warmup, stream):
@@ -315,6 +342,7 @@ def backward(args, w, plan, q, k, v, stream):
         api.sta_backward_plan(plan, q, k, v, out, g, lse, scale=w.scale, dq=dq, dk=dk, dv=dv,
                               delta=delta, stream=stream)
 
+    fit_counts(args, step, stream)
     ms = timed(step, args.steps, args.warmup, stream)
     fwd_flops = plan.flops
     # Algorithmic backward FLOPs: five products per attended tile pair
@@ -522,6 +550,7 @@ def main():
     def step():
         api.sta_forward_plan(plan, q, k, v, out=out, scale=w.scale, layout="natural", stream=stream)
 
+    fit_counts(args, step, stream)
     ms = timed(step, args.steps, args.warmup, stream)
     tflops = flops / (ms * 1e-3) / 1e12
 
