@@ -59,10 +59,8 @@ def _run(cmd):
     return r.stdout
 
 
-def build(jobs: int | None = None, verbose: bool = False, debug: bool = False) -> str:
-    """Compile the library (debug: libsta_debug.so, with -DSTA_DEBUG)."""
-    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
-        raise RuntimeError(f"hipcc not found at {HIPCC}")
+def _plan(debug: bool):
+    """Compile commands, objects and output library of one variant."""
     bdir = BUILD + ("_debug" if debug else "")
     os.makedirs(bdir, exist_ok=True)
     extra = ["-DSTA_DEBUG"] if debug else []
@@ -75,19 +73,41 @@ def build(jobs: int | None = None, verbose: bool = False, debug: bool = False) -
         o = os.path.join(bdir, s + ".o")
         cmds.append([CXX, *CXX_FLAGS, *extra, "-c", os.path.join(CSRC, s), "-o", o])
         objs.append(o)
-    jobs = jobs or min(8, len(cmds))
-    with ThreadPoolExecutor(jobs) as ex:
-        outs = list(ex.map(_run, cmds))
-    if verbose:
-        for c, o in zip(cmds, outs):
-            print(" ".join(c))
-            if o.strip():
-                print(o)
-    out = LIB_DEBUG if debug else LIB
+    return cmds, objs, (LIB_DEBUG if debug else LIB)
+
+
+def _link(objs, out):
     tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, out)
-    return out
+
+
+def build_variants(variants=(False, True), jobs: int | None = None, verbose: bool = False) -> list:
+    """Compile the given variants (False: libsta.so, True: libsta_debug.so)
+    in one pool of compiler processes, the kernel files (the longest
+    compiles) first, then link each."""
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    plans = [_plan(d) for d in variants]
+    cmds = [c for cs, _, _ in plans for c in cs]
+    slow = ("sta_forward.hip", "sta_backward.hip")
+    order = sorted(range(len(cmds)), key=lambda i: 0 if any(x in cmds[i][-3] for x in slow) else 1)
+    jobs = jobs or max(1, min(16, os.cpu_count() or 1, len(cmds)))
+    with ThreadPoolExecutor(jobs) as ex:
+        outs = dict(zip(order, ex.map(_run, [cmds[i] for i in order])))
+    if verbose:
+        for i, c in enumerate(cmds):
+            print(" ".join(c))
+            if outs[i].strip():
+                print(outs[i])
+    for _, objs, out in plans:
+        _link(objs, out)
+    return [out for _, _, out in plans]
+
+
+def build(jobs: int | None = None, verbose: bool = False, debug: bool = False) -> str:
+    """Compile the library (debug: libsta_debug.so, with -DSTA_DEBUG)."""
+    return build_variants((debug,), jobs, verbose)[0]
 
 
 def main(argv=None):
