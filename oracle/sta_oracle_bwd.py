@@ -87,15 +87,18 @@ def masked_attention_backward(q, k, v, g, mask, scale):
 
 
 def sta_backward_explicit(q, k, v, g, video: Sequence[int], tile: Sequence[int], windows,
-                          scale: float | None = None, coords: np.ndarray | None = None):
+                          scale: float | None = None, coords: np.ndarray | None = None,
+                          partial: bool = False):
     """STA forward and backward by the explicit N x N mask (small inputs).
 
     q, k, v, g: [B, heads, N, D]; token n sits at coords[n] (natural raster
-    order when coords is None).  Returns a dict of float64 arrays:
+    order when coords is None).  partial: extents need not be multiples of
+    the tile (the forward oracle's reading R11: the last tile of an axis
+    holds only the tokens that exist).  Returns a dict of float64 arrays:
     o, dq, dk, dv [B, heads, N, D] and lse [B, heads, N].
     """
     B, heads, N, D = q.shape
-    grid = F.tile_grid(video, tile)
+    grid = F.tile_grid(video, tile, partial)
     if coords is None:
         coords = F.natural_coords(video)
     if scale is None:
@@ -130,15 +133,16 @@ def _rows(x):
 
 def sta_backward_query_tiles(q, k, v, g, tile, window, head: int,
                              query_tiles: Iterable[Sequence[int]], scale: float | None = None,
-                             batch: int = 0):
+                             batch: int = 0, partial: bool = False):
     """lse and dq of selected query tiles of one head (large inputs).
 
     Inputs in natural layout [B, heads, T, H, W, D].  A query's gradient
     needs only its own window (the box of tokens of its key tiles).
-    Returns a list of (lse [tT, tH, tW], dq [tT, tH, tW, D]) in float64.
+    Returns a list of (lse [tT, tH, tW], dq [tT, tH, tW, D]) in float64
+    (smaller for a partial tile: the slices stop at the video's end).
     """
     _, _, T, H, W, D = q.shape
-    grid = F.tile_grid((T, H, W), tile)
+    grid = F.tile_grid((T, H, W), tile, partial)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out = []
@@ -148,7 +152,8 @@ def sta_backward_query_tiles(q, k, v, g, tile, window, head: int,
         vw = _rows(_window_slice(v, c, tile, window, grid, batch, head))
         mask = np.ones((qt.shape[0], kw.shape[0]), dtype=bool)
         _, lse, dq, _, _ = masked_attention_backward(qt, kw, vw, gt, mask, scale)
-        out.append((lse.reshape(tile), dq.reshape(*tile, D)))
+        shape = _tile_slice(q, c, tile, batch, head).shape[:3]
+        out.append((lse.reshape(shape), dq.reshape(*shape, D)))
     return out
 
 
@@ -165,17 +170,18 @@ def query_tiles_seeing(key_tile: Sequence[int], window: Sequence[int], grid: Seq
 
 def sta_backward_key_tiles(q, k, v, g, tile, window, head: int,
                            key_tiles: Iterable[Sequence[int]], scale: float | None = None,
-                           batch: int = 0):
+                           batch: int = 0, partial: bool = False):
     """dk and dv of selected key tiles of one head (large inputs).
 
     A key tile receives gradient from every query tile whose window holds
     it.  For each such query tile the row statistics (lse and
     sum_l P_il dP_il) are taken over that query tile's whole window; the
     probabilities and score gradients are then formed for the key tile's
-    columns alone.  Returns a list of (dk, dv), each [tT, tH, tW, D].
+    columns alone.  Returns a list of (dk, dv), each [tT, tH, tW, D]
+    (smaller for a partial tile).
     """
     _, _, T, H, W, D = q.shape
-    grid = F.tile_grid((T, H, W), tile)
+    grid = F.tile_grid((T, H, W), tile, partial)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out = []
@@ -196,5 +202,6 @@ def sta_backward_key_tiles(q, k, v, g, tile, window, head: int,
             dz = p * (gt @ vt.T - delta)
             dv += p.T @ gt
             dk += scale * (dz.T @ qt)
-        out.append((dk.reshape(*tile, D), dv.reshape(*tile, D)))
+        shape = _tile_slice(k, kc, tile, batch, head).shape[:3]
+        out.append((dk.reshape(*shape, D), dv.reshape(*shape, D)))
     return out

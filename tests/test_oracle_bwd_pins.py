@@ -25,11 +25,17 @@ from oracle import sta_oracle as F
 from oracle import sta_oracle_bwd as O
 
 
-def rand_case(rng, max_tokens=72):
+def rand_case(rng, max_tokens=72, partial=False):
+    """Random video, tile and two heads' windows; with partial, at least one
+    extent is not a multiple of its tile."""
     while True:
         tile = tuple(int(x) for x in rng.integers(1, 4, size=3))
         grid = tuple(int(x) for x in rng.integers(1, 5, size=3))
         video = tuple(t * g for t, g in zip(tile, grid))
+        if partial:
+            video = tuple(max(1, e - int(rng.integers(0, t))) for e, t in zip(video, tile))
+            if all(e % t == 0 for e, t in zip(video, tile)):
+                continue
         if video[0] * video[1] * video[2] <= max_tokens:
             break
     windows = [tuple(int(x) for x in rng.integers(1, 5, size=3)) for _ in range(2)]
@@ -48,18 +54,19 @@ def torch_attention_grads(q, k, v, g, scale):
 # The pin set, parameterised by the oracle module so that mutants can be run
 # ---------------------------------------------------------------------------
 
-def pin_finite_differences(mod, cases=3, seed=5):
+def pin_finite_differences(mod, cases=3, seed=5, partial=False):
     rng = np.random.default_rng(seed)
     fails = []
     for _ in range(cases):
-        video, tile, windows = rand_case(rng)
+        video, tile, windows = rand_case(rng, partial=partial)
         N, D = video[0] * video[1] * video[2], 3
         q, k, v, g = (rng.standard_normal((1, 2, N, D)) for _ in range(4))
         scale = 0.7
-        got = mod.sta_backward_explicit(q, k, v, g, video, tile, windows, scale=scale)
+        got = mod.sta_backward_explicit(q, k, v, g, video, tile, windows, scale=scale, partial=partial)
 
         def loss(qq, kk, vv):
-            return float((F.sta_forward_explicit(qq, kk, vv, video, tile, windows, scale=scale) * g).sum())
+            return float((F.sta_forward_explicit(qq, kk, vv, video, tile, windows, scale=scale,
+                                                 partial=partial) * g).sum())
 
         eps = 1e-6
         for name, idx in (("dq", 0), ("dk", 1), ("dv", 2)):
@@ -72,10 +79,16 @@ def pin_finite_differences(mod, cases=3, seed=5):
                 num[pos] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
             if not np.allclose(got[name], num, rtol=1e-6, atol=1e-7):
                 fails.append((name, video, tile, windows, float(np.abs(got[name] - num).max())))
-        if not np.allclose(got["o"], F.sta_forward_explicit(q, k, v, video, tile, windows, scale=scale),
+        if not np.allclose(got["o"], F.sta_forward_explicit(q, k, v, video, tile, windows, scale=scale,
+                                                            partial=partial),
                            rtol=0, atol=1e-12):
             fails.append(("o", video, tile, windows))
     return fails
+
+
+def pin_finite_differences_partial(mod):
+    """The same finite differences on grids whose last tiles are partial."""
+    return pin_finite_differences(mod, cases=3, seed=6, partial=True)
 
 
 def pin_dense_blockdiag_and_lse(mod, seed=11):
@@ -151,24 +164,26 @@ def pin_closed_forms_and_invariants(mod, seed=13):
     return fails
 
 
-def pin_tile_functions(mod, cases=3, seed=17):
+def pin_tile_functions(mod, cases=3, seed=17, partial=False):
     rng = np.random.default_rng(seed)
     fails = []
     for _ in range(cases):
-        video, tile, windows = rand_case(rng, max_tokens=120)
+        video, tile, windows = rand_case(rng, max_tokens=120, partial=partial)
         N, D = video[0] * video[1] * video[2], 3
         q, k, v, g = (rng.standard_normal((1, 2, N, D)) for _ in range(4))
         scale = 0.9
-        want = mod.sta_backward_explicit(q, k, v, g, video, tile, windows, scale=scale)
-        grid = F.tile_grid(video, tile)
+        want = mod.sta_backward_explicit(q, k, v, g, video, tile, windows, scale=scale, partial=partial)
+        grid = F.tile_grid(video, tile, partial)
         T, H, W = video
         q6, k6, v6, g6 = (x.reshape(1, 2, T, H, W, D) for x in (q, k, v, g))
         tiles = list(np.ndindex(*grid))
         for h in range(2):
             full = {n: np.zeros((T, H, W, D)) for n in ("dq", "dk", "dv")}
             lse = np.zeros((T, H, W))
-            qres = mod.sta_backward_query_tiles(q6, k6, v6, g6, tile, windows[h], h, tiles, scale=scale)
-            kres = mod.sta_backward_key_tiles(q6, k6, v6, g6, tile, windows[h], h, tiles, scale=scale)
+            qres = mod.sta_backward_query_tiles(q6, k6, v6, g6, tile, windows[h], h, tiles, scale=scale,
+                                                partial=partial)
+            kres = mod.sta_backward_key_tiles(q6, k6, v6, g6, tile, windows[h], h, tiles, scale=scale,
+                                              partial=partial)
             for c, (l, dq), (dk, dv) in zip(tiles, qres, kres):
                 sl = tuple(slice(c[d] * tile[d], (c[d] + 1) * tile[d]) for d in range(3))
                 lse[sl], full["dq"][sl], full["dk"][sl], full["dv"][sl] = l, dq, dk, dv
@@ -180,8 +195,13 @@ def pin_tile_functions(mod, cases=3, seed=17):
     return fails
 
 
-ALL_PINS = [pin_finite_differences, pin_dense_blockdiag_and_lse, pin_closed_forms_and_invariants,
-            pin_tile_functions]
+def pin_tile_functions_partial(mod):
+    """The per-tile functions against the explicit one on partial grids."""
+    return pin_tile_functions(mod, cases=3, seed=18, partial=True)
+
+
+ALL_PINS = [pin_finite_differences, pin_finite_differences_partial, pin_dense_blockdiag_and_lse,
+            pin_closed_forms_and_invariants, pin_tile_functions, pin_tile_functions_partial]
 
 
 def run_pins(mod):
@@ -214,6 +234,14 @@ def test_tile_functions_equal_explicit():
     assert pin_tile_functions(O) == []
 
 
+def test_finite_differences_partial_tiles():
+    assert pin_finite_differences_partial(O) == []
+
+
+def test_tile_functions_equal_explicit_partial_tiles():
+    assert pin_tile_functions_partial(O) == []
+
+
 def test_query_tiles_seeing_is_the_inverse_of_the_window():
     rng = np.random.default_rng(3)
     for _ in range(20):
@@ -243,6 +271,9 @@ MUTANTS = [
     ("key-tile delta over the key tile", "dz = p * (gt @ vt.T - delta)",
      "dz = p * (gt @ vt.T - (p * (gt @ vt.T)).sum(axis=1, keepdims=True))"),
     ("inverse strict bound", "box[d][0] <= key_tile[d] < box[d][1]", "box[d][0] <= key_tile[d] <= box[d][1]"),
+    ("partial grid floored", "grid = F.tile_grid(video, tile, partial)",
+     "grid = tuple(max(1, e // t) for e, t in zip(video, tile))"),
+    ("partial query-tile shape", "shape = _tile_slice(q, c, tile, batch, head).shape[:3]", "shape = tuple(tile)"),
 ]
 
 
