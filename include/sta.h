@@ -120,11 +120,12 @@ sta_status sta_plan_create(int batch, int heads, int T, int H, int W, const int 
  * open; reading used: an axis then has ceil(extent / tile) tiles, its last
  * tile partial, windows and tile geometry unchanged, and only tokens that
  * exist take part -- the same as padding the video to whole tiles and
- * masking the padded keys).  Such a plan supports sta_forward_plan and
- * sta_forward_plan_lse in STA_LAYOUT_NATURAL only; sta_plan_perm,
- * sta_tile_reorder/unreorder, the tile-major layout and sta_backward_plan
- * return STA_ERR_UNSUPPORTED for it.  Its info.flops counts whole tiles (the
- * work performed).  STA_ERR_ARG for unknown flags. */
+ * masking the padded keys).  Such a plan supports sta_forward_plan,
+ * sta_forward_plan_lse and sta_backward_plan in STA_LAYOUT_NATURAL only
+ * (the gradients of tokens that do not exist are not defined and nothing
+ * is written for them); sta_plan_perm, sta_tile_reorder/unreorder and the
+ * tile-major layout return STA_ERR_UNSUPPORTED for it.  Its info.flops
+ * counts whole tiles (the work performed).  STA_ERR_ARG for unknown flags. */
 sta_status sta_plan_create_ex(int batch, int heads, int T, int H, int W, const int tile[3],
                               const int *window, int head_dim, int flags, sta_plan **out);
 
@@ -319,9 +320,12 @@ sta_status sta_forward_plan_noalloc(const sta_plan *plan, const void *q, const v
  * range, nearest-even for fp32), and P and dS are rounded to fp16.  Entries
  * of q, k, v and dout and the products dS must lie within the fp16 range.
  * Deterministic: no atomics; dq and dk/dv come from separate kernels.
+ * Partial-tile plans (sta_plan_create_ex): natural layout only; only
+ * existing tokens take part, as in the forward.
  * Errors: STA_ERR_ARG (NULL, bad enum, scale <= 0, overlap),
  * STA_ERR_UNSUPPORTED (the plan's tile volume and window lists exceed the
- * backward kernels' LDS), STA_ERR_HIP. */
+ * backward kernels' LDS; a partial-tile plan in the tile-major layout),
+ * STA_ERR_HIP. */
 sta_status sta_backward_plan(const sta_plan *plan, const void *q, const void *k, const void *v,
                              const void *out, const void *dout, const float *lse, float *delta,
                              void *dq, void *dk, void *dv, float scale, sta_dtype in_dtype,

@@ -368,6 +368,7 @@ sta_status backward(const sta_plan *p, const void *q, const void *k, const void 
   if (layout != STA_LAYOUT_NATURAL && layout != STA_LAYOUT_TILE_MAJOR) return STA_ERR_ARG;
   if (!(scale > 0.f) || !std::isfinite(scale)) return STA_ERR_ARG;
   if (!p->bwd_ok) return STA_ERR_UNSUPPORTED;
+  if (p->partial && layout != STA_LAYOUT_NATURAL) return STA_ERR_UNSUPPORTED;   // tile-major needs whole tiles
   const size_t rows = (size_t)p->batch * p->heads * p->N;
   const size_t elems = rows * p->D;
   const size_t ib = elems * dtype_bytes(in_dtype), ob = elems * dtype_bytes(out_dtype);
@@ -396,6 +397,7 @@ sta_status backward(const sta_plan *p, const void *q, const void *k, const void 
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.base = layout == STA_LAYOUT_NATURAL ? t.base_nat : t.base_tm;
   a.off = layout == STA_LAYOUT_NATURAL ? t.off_nat : t.off_tm;
+  a.kmask = reinterpret_cast<const uint32_t *>(t.kmask);
   a.heads = p->heads;
   a.n_tiles = p->n_tiles;
   a.V = p->V;

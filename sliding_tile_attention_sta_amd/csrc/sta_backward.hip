@@ -27,6 +27,15 @@
 //     the keys' K and V in VGPRs, then dV^T += dO^T P and dK^T += Q^T dS with
 //     dO^T and Q^T read transposed from LDS.
 //
+// Extents that are not multiples of the tile (partial tiles at the far
+// edges; a separate instantiation of each kernel, PARTIAL): as in the
+// forward, only tokens that exist take part.  Rows of tile positions that
+// do not exist are clamped to the tensor for loading, the walk's validity
+// words (one per 32-token block, staged in LDS) zero P and dS of keys
+// (dQ) or queries (dK/dV) that do not exist, and nothing is stored for
+// them; such a row's own gradient is computed from clamped values and
+// dropped.
+//
 // The products run on v_mfma_f32_16x16x32_f16 with fp32 accumulation.
 // P and dS are rounded to fp16 (11 significant bits against bf16's 8); Q and
 // K are the forward's bf16 values (fp32 inputs rounded to bf16 first, so
@@ -155,10 +164,24 @@ __device__ __forceinline__ Item decode(int item, const BwdArgs &a) {
   return it;
 }
 
+// PARTIAL (extents that are not multiples of the tile): a tile-local token
+// that does not exist has a row past the tile's edge, possibly past the
+// tensor; loads take the last row instead (their values are masked), and
+// nothing is stored for it.  exists(): bit (local mod 32) of the tile's
+// validity word (local / 32).
+template <bool PARTIAL>
+__device__ __forceinline__ int clamp_row(int row, int64_t n) {
+  if constexpr (PARTIAL) return row < n ? row : (int)n - 1;
+  return row;
+}
+__device__ __forceinline__ bool exists(const uint32_t *kmask, int tile, int local, int V) {
+  return (kmask[(size_t)tile * (V / TB) + local / TB] >> (local % TB)) & 1u;
+}
+
 // ---------------------------------------------------------------------------
 // dQ: queries resident, key blocks streamed.
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool F32IN>
+template <int D, int NW, bool F32IN, bool PARTIAL>
 // Two waves per SIMD: without the hint the allocator parks the Q and dO
 // fragments in AGPRs and copies them back every step (about 100 extra VALU
 // instructions per step).  Except for one wave with D = 128 (tile volumes
@@ -178,10 +201,12 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
   constexpr int DC = D / 32;
   constexpr int DB = D / 16;
 
-  // LDS: K stages 0/1, V stages 0/1, tile-local offsets, key-tile base rows.
+  // LDS: K stages 0/1, V stages 0/1, tile-local offsets, key-tile base rows
+  // (PARTIAL: then the validity word of every 32-key block of the walk).
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int *off_l = reinterpret_cast<int *>(smem + 4 * ST);
   int *lb_l = off_l + a.V;
+  uint32_t *mw_l = reinterpret_cast<uint32_t *>(lb_l + a.max_list);
 
   const int item = __builtin_amdgcn_readfirstlane(a.sched[blockIdx.x]);
   if (item < 0) return;
@@ -196,6 +221,10 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
   for (int i = tid; i < nl; i += NT) {
     STA_CHECK(a.dbg, (unsigned)a.list_idx[l0 + i] < (unsigned)a.n_tiles && i < a.max_list, 1);
     lb_l[i] = a.base[a.list_idx[l0 + i]];
+  }
+  if constexpr (PARTIAL) {
+    const int words = a.V / TB;
+    for (int i = tid; i < nl * words; i += NT) mw_l[i] = a.kmask[(size_t)a.list_idx[l0 + i / words] * words + i % words];
   }
 
   const size_t plane = (size_t)it.bh * a.N;
@@ -214,7 +243,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
   float lse2[2], dl[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int row = qbase + off_l[qloc0 + 16 * j + l16];
+    const int row = clamp_row<PARTIAL>(qbase + off_l[qloc0 + 16 * j + l16], a.N);
     STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 2);
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
@@ -241,8 +270,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (CHUNKS < NT && c >= CHUNKS) break;
-      STA_CHECK(a.dbg, (unsigned)(tb + off_l[u * TB + c / (D / 8)]) < (unsigned)a.N, 2);
-      const size_t e = (size_t)(tb + off_l[u * TB + c / (D / 8)]) * D + (c % (D / 8)) * 8;
+      const int row = clamp_row<PARTIAL>(tb + off_l[u * TB + c / (D / 8)], a.N);
+      STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 2);
+      const size_t e = (size_t)row * D + (c % (D / 8)) * 8;
       dk[i] = load_raw<F32IN>(kg + e * EB);
       dv[i] = load_raw<F32IN>(vg + e * EB);
     }
@@ -305,6 +335,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
         }
       }
     // dS^T in fp16, slots: keys 4g + r (kb 0) and 16 + 4g + r (kb 1).
+    // PARTIAL: keys that do not exist get dS = 0.
+    const uint32_t kw = PARTIAL ? mw_l[s] : 0u;
     f16x8 dsf[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -313,7 +345,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r], sl2e, -lse2[j]));
-          dsf[j][kb * 4 + r] = (_Float16)(p * (dp[kb][j][r] - dl[j]));
+          float ds = p * (dp[kb][j][r] - dl[j]);
+          if constexpr (PARTIAL) ds = (kw >> (kb * 16 + 4 * g + r)) & 1u ? ds : 0.f;
+          dsf[j][kb * 4 + r] = (_Float16)ds;
         }
     // dQ^T += K^T dS^T.
 #pragma unroll
@@ -340,7 +374,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
   void *dq = static_cast<char *>(a.dq) + plane * D * (a.f32_out ? 4 : 2);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int row = qbase + off_l[qloc0 + 16 * j + l16];
+    const int ql = qloc0 + 16 * j + l16;
+    if (PARTIAL && !exists(a.kmask, it.tile, ql, a.V)) continue;   // no such query
+    const int row = qbase + off_l[ql];
     STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 3);
 #pragma unroll
     for (int b = 0; b < DB; ++b) store4(dq, (size_t)row * D + 16 * b + 4 * g, acc[b][j] * a.scale, a.f32_out);
@@ -362,7 +398,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
 // block s-1 and block s+1 is written), the P exchange through a two-stage
 // buffer; one barrier per step.
 // ---------------------------------------------------------------------------
-template <int D, int NP, bool F32IN>
+template <int D, int NP, bool F32IN, bool PARTIAL>
 __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NT = NP * 128;
   constexpr int KPI = 32 * NP;
@@ -379,12 +415,14 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
 
   // LDS: Q stages 0..2, dO stages 0..2, row statistics [stage][lse*log2e |
   // delta][32], P exchange stages 0/1 [pair][kb][lane] (16 B), tile-local
-  // offsets, query-tile base rows.
+  // offsets, query-tile base rows (PARTIAL: then the validity word of every
+  // 32-query block of the walk).
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float *stat = reinterpret_cast<float *>(smem + 6 * ST);
   char *pbuf = reinterpret_cast<char *>(stat + 3 * 2 * TB);
   int *off_l = reinterpret_cast<int *>(pbuf + 2 * PB);
   int *lb_l = off_l + a.V;
+  uint32_t *mw_l = reinterpret_cast<uint32_t *>(lb_l + a.max_list);
 
   const int item = __builtin_amdgcn_readfirstlane(a.sched[blockIdx.x]);
   if (item < 0) return;
@@ -402,6 +440,10 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
     STA_CHECK(a.dbg, (unsigned)a.list_idx[l0 + i] < (unsigned)a.n_tiles && i < a.max_list, 1);
     lb_l[i] = a.base[a.list_idx[l0 + i]];
   }
+  if constexpr (PARTIAL) {
+    const int words = a.V / TB;
+    for (int i = tid; i < nl * words; i += NT) mw_l[i] = a.kmask[(size_t)a.list_idx[l0 + i / words] * words + i % words];
+  }
 
   const size_t plane = (size_t)it.bh * a.N;
   const char *qg = static_cast<const char *>(a.q) + plane * D * EB;
@@ -418,7 +460,7 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
     const char *src = static_cast<const char *>(wa ? a.k : a.v) + plane * D * EB;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int row = kbase + off_l[kloc0 + 16 * kb + l16];
+      const int row = clamp_row<PARTIAL>(kbase + off_l[kloc0 + 16 * kb + l16], a.N);
       STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 2);
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
@@ -441,13 +483,14 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (CHUNKS < NT && c >= CHUNKS) break;
-      STA_CHECK(a.dbg, (unsigned)(tb + off_l[u * TB + c / (D / 8)]) < (unsigned)a.N, 2);
-      const size_t e = (size_t)(tb + off_l[u * TB + c / (D / 8)]) * D + (c % (D / 8)) * 8;
+      const int row = clamp_row<PARTIAL>(tb + off_l[u * TB + c / (D / 8)], a.N);
+      STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 2);
+      const size_t e = (size_t)row * D + (c % (D / 8)) * 8;
       rq[i] = load_raw<F32IN>(qg + e * EB);
       rg[i] = load_raw<F32IN>(gg + e * EB);
     }
     if (tid < 2 * TB) {
-      const int row = tb + off_l[u * TB + (tid & (TB - 1))];
+      const int row = clamp_row<PARTIAL>(tb + off_l[u * TB + (tid & (TB - 1))], a.N);
       STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 2);
       rs = tid < TB ? lse[row] * kLog2e : delta[row];
     }
@@ -509,7 +552,9 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
           for (int kb = 0; kb < 2; ++kb)
             t[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, frag[kb][c], t[j][kb], 0, 0, 0);
         }
-      // Slots 4j + r of each 16-key block: queries 16j + 4g + r.
+      // Slots 4j + r of each 16-key block: queries 16j + 4g + r.  PARTIAL:
+      // queries that do not exist get P = 0 and dS = 0.
+      const uint32_t qw = PARTIAL ? mw_l[wa ? s : s - 1] : 0u;
       f16x8 w[2];
       if (wa) {
         // P = exp2(S scale log2(e) - lse log2(e)), to registers and LDS.
@@ -519,8 +564,11 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              w[kb][4 * j + r] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(t[j][kb][r], sl2e, -L[r]));
+            for (int r = 0; r < 4; ++r) {
+              float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j][kb][r], sl2e, -L[r]));
+              if constexpr (PARTIAL) pv = (qw >> (16 * j + 4 * g + r)) & 1u ? pv : 0.f;
+              w[kb][4 * j + r] = (_Float16)pv;
+            }
         }
         *reinterpret_cast<f16x8 *>(pex) = w[0];
         *reinterpret_cast<f16x8 *>(pex + 64 * 16) = w[1];
@@ -533,8 +581,15 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
           const f32x4 Dl = *reinterpret_cast<const f32x4 *>(ls + TB + 16 * j + 4 * g);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            w[0][4 * j + r] = (_Float16)((float)p0[4 * j + r] * (t[j][0][r] - Dl[r]));
-            w[1][4 * j + r] = (_Float16)((float)p1[4 * j + r] * (t[j][1][r] - Dl[r]));
+            float d0 = (float)p0[4 * j + r] * (t[j][0][r] - Dl[r]);
+            float d1 = (float)p1[4 * j + r] * (t[j][1][r] - Dl[r]);
+            if constexpr (PARTIAL) {
+              const bool ok = (qw >> (16 * j + 4 * g + r)) & 1u;
+              d0 = ok ? d0 : 0.f;
+              d1 = ok ? d1 : 0.f;
+            }
+            w[0][4 * j + r] = (_Float16)d0;
+            w[1][4 * j + r] = (_Float16)d1;
           }
         }
       }
@@ -558,7 +613,9 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
   const float mul = wa ? 1.f : a.scale;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int row = kbase + off_l[kloc0 + 16 * kb + l16];
+    const int kl = kloc0 + 16 * kb + l16;
+    if (PARTIAL && !exists(a.kmask, it.tile, kl, a.V)) continue;   // no such key
+    const int row = kbase + off_l[kl];
     STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 3);
 #pragma unroll
     for (int b = 0; b < DB; ++b) store4(dst, (size_t)row * D + 16 * b + 4 * g, acc[b][kb] * mul, a.f32_out);
@@ -577,19 +634,31 @@ hipError_t launch_lds(K kern, int blocks, int threads, size_t lds, const BwdArgs
   return hipGetLastError();
 }
 
+// PARTIAL adds the walk's validity words (one per 32-token block).
 template <int D, int NW>
 hipError_t dq_one(const BwdArgs &a, bool f32_in, hipStream_t s) {
-  const size_t lds = (size_t)4 * TB * bwd_stride(D) + 4 * (a.V + a.max_list);
-  if (f32_in) return launch_lds(sta_bwd_dq_kernel<D, NW, true>, a.n_blocks, NW * 64, lds, a, s);
-  return launch_lds(sta_bwd_dq_kernel<D, NW, false>, a.n_blocks, NW * 64, lds, a, s);
+  const bool part = a.kmask != nullptr;
+  const size_t lds = (size_t)4 * TB * bwd_stride(D) + 4 * (a.V + a.max_list) +
+                     (part ? (size_t)4 * a.max_list * (a.V / TB) : 0);
+  if (part) {
+    if (f32_in) return launch_lds(sta_bwd_dq_kernel<D, NW, true, true>, a.n_blocks, NW * 64, lds, a, s);
+    return launch_lds(sta_bwd_dq_kernel<D, NW, false, true>, a.n_blocks, NW * 64, lds, a, s);
+  }
+  if (f32_in) return launch_lds(sta_bwd_dq_kernel<D, NW, true, false>, a.n_blocks, NW * 64, lds, a, s);
+  return launch_lds(sta_bwd_dq_kernel<D, NW, false, false>, a.n_blocks, NW * 64, lds, a, s);
 }
 
 template <int D, int NP>
 hipError_t dkdv_one(const BwdArgs &a, bool f32_in, hipStream_t s) {
+  const bool part = a.kmask != nullptr;
   const size_t lds = (size_t)6 * TB * bwd_stride(D) + 4 * 6 * TB + 2 * NP * 2 * 64 * 16 +
-                     4 * (a.V + a.max_list);
-  if (f32_in) return launch_lds(sta_bwd_dkdv_kernel<D, NP, true>, a.n_blocks, NP * 128, lds, a, s);
-  return launch_lds(sta_bwd_dkdv_kernel<D, NP, false>, a.n_blocks, NP * 128, lds, a, s);
+                     4 * (a.V + a.max_list) + (part ? (size_t)4 * a.max_list * (a.V / TB) : 0);
+  if (part) {
+    if (f32_in) return launch_lds(sta_bwd_dkdv_kernel<D, NP, true, true>, a.n_blocks, NP * 128, lds, a, s);
+    return launch_lds(sta_bwd_dkdv_kernel<D, NP, false, true>, a.n_blocks, NP * 128, lds, a, s);
+  }
+  if (f32_in) return launch_lds(sta_bwd_dkdv_kernel<D, NP, true, false>, a.n_blocks, NP * 128, lds, a, s);
+  return launch_lds(sta_bwd_dkdv_kernel<D, NP, false, false>, a.n_blocks, NP * 128, lds, a, s);
 }
 
 }  // namespace

@@ -54,9 +54,11 @@ constexpr long long kMaxLds = 160 * 1024;
 // between its wave pairs (up to 6 pairs x 2 KiB).  Both keep the tile-local
 // row offsets and the item's tile base rows.  The dK/dV layout is the larger.
 constexpr int bwd_stride(int head_dim) { return 2 * head_dim + 32; }
-constexpr long long bwd_lds_bytes(int head_dim, long long tile_tokens, long long max_list) {
+// With partial tiles both add one validity word per 32-token block of their
+// walk.
+constexpr long long bwd_lds_bytes(int head_dim, long long tile_tokens, long long max_list, bool partial) {
   return 3LL * 2 * kKeyBlock * bwd_stride(head_dim) + 3LL * 2 * kKeyBlock * 4 + 2LL * 6 * 2048 +
-         4LL * (tile_tokens + max_list);
+         4LL * (tile_tokens + max_list) + (partial ? 4LL * max_list * (tile_tokens / kKeyBlock) : 0);
 }
 
 struct DeviceTables {

@@ -72,6 +72,7 @@ struct BwdArgs {
   const int32_t *list_idx;
   const int32_t *base;     // n_tiles: first token row of each tile in the tensors' layout
   const int32_t *off;      // tile_tokens: row offset of each tile-local token
+  const uint32_t *kmask;   // partial plans: n_tiles * V/32 token validity words (else null)
   int32_t heads, n_tiles, V, subs;
   int64_t N;
   float scale;             // softmax scale

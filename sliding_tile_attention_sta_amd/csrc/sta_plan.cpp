@@ -436,7 +436,7 @@ sta_status build_plan(int batch, int heads, int T, int H, int W, const int tile[
     p->bwd_k_pairs = p->V % 192 == 0 ? 6 : p->V % 128 == 0 ? 4 : 1;
     p->bwd_q_subs = p->V / (32 * p->bwd_q_waves);
     p->bwd_k_subs = p->V / (32 * p->bwd_k_pairs);
-    p->bwd_ok = !p->partial && bwd_lds_bytes(head_dim, p->V, std::max(p->max_nkv, p->max_nq)) <= kMaxLds;
+    p->bwd_ok = bwd_lds_bytes(head_dim, p->V, std::max(p->max_nkv, p->max_nq), p->partial) <= kMaxLds;
     if (p->bwd_ok) {
       p->sched_dq = build_schedule(p, p->kv_off, p->bwd_q_subs);
       p->sched_dkdv = build_schedule(p, p->q_off, p->bwd_k_subs);

@@ -356,10 +356,11 @@ def test_inverse_lists_match_oracle(name):
             assert p.q_tiles(h, kt) == want
 
 
-@pytest.mark.parametrize("name", ["tiny", "small", "720p", "mixed"])
+@pytest.mark.parametrize("name", ["tiny", "small", "720p", "mixed", "720p-exact", "partial-small"])
 def test_backward_schedules_cover_every_item_once(name):
     w = WORKLOADS[name]
-    p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim)
+    partial = any(e % t for e, t in zip(w.video, w.tile))
+    p = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim, partial_tiles=partial)
     info = p.info
     assert info.bwd_supported == 1
     for which, count, per in ((0, info.bwd_items_dq, info.bwd_queries_per_item),
@@ -469,7 +470,7 @@ def test_partial_plan_geometry_and_unsupported_paths():
     info = p.info
     grid = O.tile_grid(video, tile, partial=True)
     assert tuple(info.grid) == grid == (5, 6, 10)
-    assert info.partial_tiles == 1 and info.bwd_supported == 0
+    assert info.partial_tiles == 1 and info.bwd_supported == 1
     nT, nH, nW = grid
     for qt in range(0, nT * nH * nW, 3):
         c = (qt // (nH * nW), (qt // nW) % nH, qt % nW)
@@ -485,8 +486,12 @@ def test_partial_plan_geometry_and_unsupported_paths():
     assert lib.sta_tile_reorder(p.handle, q, o, 0, None) == L.STA_ERR_UNSUPPORTED
     assert lib.sta_forward_plan(p.handle, q, k, v, o, 0.125, 0, 1, L.STA_LAYOUT_TILE_MAJOR, None) == L.STA_ERR_UNSUPPORTED
     g, lse, dl, dq, dk, dv = (P(i << 40) for i in range(5, 11))
-    assert lib.sta_backward_plan(p.handle, q, k, v, o, g, lse, dl, dq, dk, dv, 0.125, 0, 1, 1, 0,
-                                 None) == L.STA_ERR_UNSUPPORTED
+    # the backward runs on partial plans in the natural layout only
+    assert lib.sta_backward_plan(p.handle, q, k, v, o, g, lse, dl, dq, dk, dv, 0.125, 0, 1, 1,
+                                 L.STA_LAYOUT_TILE_MAJOR, None) == L.STA_ERR_UNSUPPORTED
+    for which, per in ((0, info.bwd_queries_per_item), (1, info.bwd_keys_per_item)):
+        s = p.schedule_bwd(which).numpy()
+        assert sorted(s[s >= 0].tolist()) == list(range(2 * info.n_tiles * (info.tile_tokens // per)))
     h = ctypes.c_void_p()
     assert lib.sta_plan_create_ex(1, 2, *video, _ints(list(tile)), _ints(list(window) * 2), 128, 6,
                                   ctypes.byref(h)) == L.STA_ERR_ARG

@@ -53,7 +53,7 @@ def run(l, w, layout, noalloc=False):
         st = l.sta_forward_plan_noalloc(h, P(q), P(k), P(v), P(out2), None, w.scale, dt, L.STA_F32, layout, None)
         assert st == L.STA_OK, st
         res.append(out2)
-    if info.bwd_supported and not partial and not info.swa:
+    if info.bwd_supported and not info.swa:
         g = make_grad_out(w, "cuda")
         delta = torch.empty_like(lse)
         grads = [torch.full(q.shape, float("nan"), device="cuda") for _ in range(3)]
