@@ -325,12 +325,17 @@ sta_status forward(const sta_plan *p, const void *q, const void *k, const void *
   a.n_blocks = (int32_t)p->sched.size();
   a.max_nkv = p->max_nkv;
   a.lse = lse;
-  // Per-step addressing of K and V: whole tiles, blocks that are a first row
-  // plus per-position offsets, a step table that fits in LDS beside the
-  // stages, and tensors of one (batch, head) below 2 GiB (32-bit offsets).
-  a.sep = !p->partial && !p->swa && (layout == STA_LAYOUT_TILE_MAJOR || p->sep_nat) &&
-          fwd_lds_bytes(p->D, p->V, p->max_nkv) + fwd_lds_step_bytes(p->V, p->max_nkv) <= kMaxLds &&
-          p->N * p->D * (long long)dtype_bytes(in_dtype) < (1LL << 31);
+  // Per-step addressing of K and V: blocks that are a first row plus
+  // per-position offsets, a step table that fits in LDS beside the stages
+  // (and the validity words of partial tiles), and byte offsets below 2 GiB
+  // for every row a tile position names in one (batch, head): partial
+  // tiles name rows past the tensor, which the buffer loads' range check
+  // reads as zeros.
+  const long long last_row = p->partial ? (long long)p->base_nat.back() + p->off_nat.back() : p->N - 1;
+  a.sep = !p->swa && (layout == STA_LAYOUT_TILE_MAJOR || p->sep_nat) &&
+          fwd_lds_bytes(p->D, p->V, p->max_nkv) +
+                  (p->partial ? 2 : 1) * fwd_lds_step_bytes(p->V, p->max_nkv) <= kMaxLds &&
+          std::max<long long>(last_row + 1, p->N) * p->D * (long long)dtype_bytes(in_dtype) < (1LL << 31);
   a.kmask = reinterpret_cast<const uint32_t *>(t.kmask);
   a.swin = t.swin;
   a.T = p->T; a.H = p->H; a.W = p->W;

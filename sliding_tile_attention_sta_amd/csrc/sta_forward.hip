@@ -42,7 +42,8 @@
 //     row offset), so one kernel reads and writes either the natural
 //     [T, H, W] token order or the tile-major order.
 //   * Partial tiles (an extent that is not a multiple of its tile size; a
-//     separate instantiation, PARTIAL): rows are clamped to the tensor, the
+//     separate instantiation, PARTIAL): rows are clamped to the tensor (with
+//     per-step addressing, rows past it read as zeros instead), the
 //     scores of keys that do not exist are set to -inf from a per-tile
 //     validity bitmask (one 32-bit word per 32-key block), and queries that
 //     do not exist are not stored.  Only tiles at the video's far edges
@@ -255,8 +256,9 @@ next_item:
       mw_l[i] = a.kmask[(size_t)a.kv_idx[kv0 + i / words] * words + i % words];
   }
   // SEP: the byte offset of the first key row of every 32-key block of the
-  // walk (the rows of a block are that row plus a fixed offset per position).
-  int *stp_l = reinterpret_cast<int *>(kvb_l + a.max_nkv);
+  // walk (the rows of a block are that row plus a fixed offset per position),
+  // after the validity words when both are used.
+  int *stp_l = reinterpret_cast<int *>(kvb_l + a.max_nkv) + (PARTIAL ? a.max_nkv * (a.V / KB) : 0);
   if constexpr (SEP) {
     const int spb = a.V / KB;
     for (int i = tid; i < nkv * spb; i += NT)
@@ -348,7 +350,9 @@ next_item:
       for (int i = 0; i < CPT; ++i) {
         const int c = tid + i * NT;
         if (CHUNKS < NT && c >= CHUNKS) break;
-        STA_CHECK(a.dbg, nrow[0] >= 0 && (long long)nrow[0] + voff[i] + 8 * EB <= a.N * D * EB, 2);
+        // (PARTIAL: rows past the tensor are read as zeros by the buffer's
+        // range check, and masked)
+        STA_CHECK(a.dbg, nrow[0] >= 0 && (PARTIAL || (long long)nrow[0] + voff[i] + 8 * EB <= a.N * D * EB), 2);
         if constexpr (F32IN) {
           dst[i].x = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + nrow[0], 0, 0));
           dst[i].y = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + nrow[0] + 16, 0, 0));
@@ -947,7 +951,7 @@ template <int D, int QB, int NW, bool FI, bool FO, bool PARTIAL, bool SWA, bool 
 hipError_t launch_kernel(const FwdArgs &a, int blocks, hipStream_t s) {
   auto kern = sta_fwd_kernel<D, QB, NW, FI, FO, PARTIAL, SWA, SEP, FIXUP, MULTI>;
   const size_t lds = (size_t)fwd_lds_bytes(D, a.V, a.max_nkv) +
-                     (PARTIAL || SEP ? (size_t)fwd_lds_step_bytes(a.V, a.max_nkv) : 0);
+                     ((PARTIAL ? 1 : 0) + (SEP ? 1 : 0)) * (size_t)fwd_lds_step_bytes(a.V, a.max_nkv);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -992,7 +996,10 @@ hipError_t launch_p(const FwdArgs &a, bool f32_in, bool f32_out, hipStream_t s) 
     return f32_out ? launch_one<D, QB, NW, false, true, false, true>(a, s)
                    : launch_one<D, QB, NW, false, false, false, true>(a, s);
   }
-  if (a.kmask != nullptr) return launch_io<D, QB, NW, true>(a, f32_in, f32_out, s);
+  if (a.kmask != nullptr) {
+    if (a.sep) return launch_io<D, QB, NW, true, true>(a, f32_in, f32_out, s);
+    return launch_io<D, QB, NW, true>(a, f32_in, f32_out, s);
+  }
   if (a.sep) return launch_io<D, QB, NW, false, true>(a, f32_in, f32_out, s);
   return launch_io<D, QB, NW, false>(a, f32_in, f32_out, s);
 }
