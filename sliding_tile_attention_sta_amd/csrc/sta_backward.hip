@@ -31,10 +31,10 @@
 // edges; a separate instantiation of each kernel, PARTIAL): as in the
 // forward, only tokens that exist take part.  Rows of tile positions that
 // do not exist are clamped to the tensor for loading, the walk's validity
-// words (one per 32-token block, staged in LDS) zero P and dS of keys
-// (dQ) or queries (dK/dV) that do not exist, and nothing is stored for
-// them; such a row's own gradient is computed from clamped values and
-// dropped.
+// words (one per 32-token block, staged in LDS) zero dS of keys that do
+// not exist (dQ) and give queries that do not exist an infinite log-sum-
+// exp, so their P and dS are 0 (dK/dV), and nothing is stored for them;
+// such a row's own gradient is computed from clamped values and dropped.
 //
 // The products run on v_mfma_f32_16x16x32_f16 with fp32 accumulation.
 // P and dS are rounded to fp16 (11 significant bits against bf16's 8); Q and
@@ -335,8 +335,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
         }
       }
     // dS^T in fp16, slots: keys 4g + r (kb 0) and 16 + 4g + r (kb 1).
-    // PARTIAL: keys that do not exist get dS = 0.
-    const uint32_t kw = PARTIAL ? mw_l[s] : 0u;
+    // PARTIAL: keys that do not exist get dS = 0 (a block whose keys all
+    // exist, every block of an interior tile, skips it on a scalar branch).
     f16x8 dsf[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -345,10 +345,20 @@ __attribute__((amdgpu_waves_per_eu(NW == 1 && D == 128 ? 1 : 2, 2))) void sta_bw
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j][r], sl2e, -lse2[j]));
-          float ds = p * (dp[kb][j][r] - dl[j]);
-          if constexpr (PARTIAL) ds = (kw >> (kb * 16 + 4 * g + r)) & 1u ? ds : 0.f;
-          dsf[j][kb * 4 + r] = (_Float16)ds;
+          dsf[j][kb * 4 + r] = (_Float16)(p * (dp[kb][j][r] - dl[j]));
         }
+    if constexpr (PARTIAL) {
+      const uint32_t kw = __builtin_amdgcn_readfirstlane(mw_l[s]);
+      if (kw != 0xffffffffu) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (!((kw >> (kb * 16 + 4 * g + r)) & 1u)) dsf[j][kb * 4 + r] = (_Float16)0.f;
+      }
+    }
     // dQ^T += K^T dS^T.
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
@@ -493,6 +503,9 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
       const int row = clamp_row<PARTIAL>(tb + off_l[u * TB + (tid & (TB - 1))], a.N);
       STA_CHECK(a.dbg, (unsigned)row < (unsigned)a.N, 2);
       rs = tid < TB ? lse[row] * kLog2e : delta[row];
+      // PARTIAL: a query that does not exist gets lse = +inf, so its P (and
+      // with it dS) is exp2(-inf) = 0 in both waves of every pair.
+      if (PARTIAL && tid < TB && !((mw_l[s] >> tid) & 1u)) rs = INFINITY;
     }
   };
   auto stash = [&](int stage) {
@@ -552,9 +565,7 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
           for (int kb = 0; kb < 2; ++kb)
             t[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, frag[kb][c], t[j][kb], 0, 0, 0);
         }
-      // Slots 4j + r of each 16-key block: queries 16j + 4g + r.  PARTIAL:
-      // queries that do not exist get P = 0 and dS = 0.
-      const uint32_t qw = PARTIAL ? mw_l[wa ? s : s - 1] : 0u;
+      // Slots 4j + r of each 16-key block: queries 16j + 4g + r.
       f16x8 w[2];
       if (wa) {
         // P = exp2(S scale log2(e) - lse log2(e)), to registers and LDS.
@@ -564,11 +575,8 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j][kb][r], sl2e, -L[r]));
-              if constexpr (PARTIAL) pv = (qw >> (16 * j + 4 * g + r)) & 1u ? pv : 0.f;
-              w[kb][4 * j + r] = (_Float16)pv;
-            }
+            for (int r = 0; r < 4; ++r)
+              w[kb][4 * j + r] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(t[j][kb][r], sl2e, -L[r]));
         }
         *reinterpret_cast<f16x8 *>(pex) = w[0];
         *reinterpret_cast<f16x8 *>(pex + 64 * 16) = w[1];
@@ -581,15 +589,8 @@ __global__ __launch_bounds__(NP * 128) void sta_bwd_dkdv_kernel(BwdArgs a) {
           const f32x4 Dl = *reinterpret_cast<const f32x4 *>(ls + TB + 16 * j + 4 * g);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float d0 = (float)p0[4 * j + r] * (t[j][0][r] - Dl[r]);
-            float d1 = (float)p1[4 * j + r] * (t[j][1][r] - Dl[r]);
-            if constexpr (PARTIAL) {
-              const bool ok = (qw >> (16 * j + 4 * g + r)) & 1u;
-              d0 = ok ? d0 : 0.f;
-              d1 = ok ? d1 : 0.f;
-            }
-            w[0][4 * j + r] = (_Float16)d0;
-            w[1][4 * j + r] = (_Float16)d1;
+            w[0][4 * j + r] = (_Float16)((float)p0[4 * j + r] * (t[j][0][r] - Dl[r]));
+            w[1][4 * j + r] = (_Float16)((float)p1[4 * j + r] * (t[j][1][r] - Dl[r]));
           }
         }
       }
