@@ -6,6 +6,7 @@ tiles: max 2e-2, mean 2e-3 absolute.  The small case compares every token
 compares sampled query tiles, among them the partial ones.
 """
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -175,3 +176,22 @@ def test_720p_exact_backward_sampled_and_edges():
                     np.concatenate([r[0].reshape(-1) for r in refk]))
         _check_grad("dv", np.concatenate([sl(dv_h, c).reshape(-1) for c in kt]),
                     np.concatenate([r[1].reshape(-1) for r in refk]))
+
+
+def test_partial_autograd_function():
+    """Autograd through sta_attention on a partial-tile plan (fp32 inputs;
+    the oracle is fed them as the kernels consume them)."""
+    w = dataclasses.replace(PARTIAL_384, dtype="f32")
+    say(f"case {w.name}, fp32, autograd through sta_attention")
+    q, k, v = make_qkv(w)
+    g = make_grad_out(w)
+    plan = api.Plan(w.batch, w.heads, w.video, w.tile, w.windows, w.head_dim, partial_tiles=True)
+    qd, kd, vd = (x.cuda().requires_grad_(True) for x in (q, k, v))
+    out = api.sta_attention(qd, kd, vd, plan, scale=w.scale)
+    (out * g.cuda()).sum().backward()
+    shp = (w.batch, w.heads, w.tokens, w.head_dim)
+    cq, ck, cv, cg = _consumed(q, "qk"), _consumed(k, "qk"), _consumed(v, "v"), _consumed(g, "v")
+    ref = OB.sta_backward_explicit(*(x.reshape(shp).double().numpy() for x in (cq, ck, cv, cg)), w.video,
+                                   w.tile, w.windows, scale=w.scale, partial=True)
+    for nm, t in (("dq", qd.grad), ("dk", kd.grad), ("dv", vd.grad)):
+        _check_grad(nm, t.reshape(shp).cpu().numpy(), ref[nm])
