@@ -5,8 +5,9 @@ variants and every backward wave layout run), a tile grid of 1 to 4 tiles
 per axis, sometimes extents that are not multiples of the tile (partial
 tiles), 1 to 3 heads with their own windows of 1 to grid + 1
 tiles (wider than the grid is clamped), head_dim 64 or 128, bf16 or fp32
-inputs and batch 1 or 2; two fixed cases add 384-token tiles on a multi-tile
-grid at d64 (bf16) and d128 (fp32).  Every token is compared with the
+inputs and batch 1 or 2; fixed cases add 384-token tiles on a multi-tile
+grid at d64 (bf16) and d128 (fp32), and partial tiles on every axis with
+384-token tiles at d64 and 128-token tiles at d128.  Every token is compared with the
 oracles: the forward output to max 2e-2 / mean 2e-3 absolute; the row
 log-sum-exp to 1e-3; each gradient to max 2e-2 / mean 2e-3 of its rms, with
 the backward oracle fed the values the kernels consume for fp32 inputs
@@ -67,6 +68,10 @@ CASES = random_cases() + [
     # 384-query forward and the 4-wave dQ / 6-pair dK/dV kernels)
     (Workload("fixed-384-d64", 230, (12, 16, 16), (6, 8, 8), ((1, 2, 2), (2, 1, 2)), 64, "bf16"), False),
     (Workload("fixed-384-f32", 231, (12, 16, 16), (6, 8, 8), ((2, 2, 1), (1, 1, 1)), 128, "f32"), False),
+    # partial tiles on every axis with the 384-token kernels at d64 bf16, and
+    # with 128-token tiles (4-wave dQ, 4-pair dK/dV) at d128 bf16
+    (Workload("fixed-384-d64-partial", 232, (11, 13, 21), (6, 8, 8), ((2, 2, 3), (1, 2, 1)), 64, "bf16"), True),
+    (Workload("fixed-128-partial", 233, (5, 15, 13), (2, 8, 8), ((3, 2, 2), (2, 3, 1)), 128, "bf16"), True),
 ]
 
 
