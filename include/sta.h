@@ -359,8 +359,11 @@ sta_status sta_forward(const void *q, const void *k, const void *v, void *out, i
  * heads * n_cand doubles.  Runs the forward once with the full window and
  * once per candidate (all heads at once) on stream, with fp32 outputs; the
  * library allocates two fp32 [batch, heads, N, head_dim] device buffers for
- * the call and frees them, and the call synchronises stream.
- * Errors: as sta_plan_create and sta_forward_plan; STA_ERR_ALLOC. */
+ * the call and frees them, and the call synchronises stream.  Extents that
+ * are not multiples of the tile use plans with partial tiles
+ * (STA_PLAN_PARTIAL_TILES of sta_plan_create_ex; grid = ceil(extent /
+ * tile), natural layout only: STA_ERR_UNSUPPORTED for the tile-major one).
+ * Errors: as sta_plan_create_ex and sta_forward_plan; STA_ERR_ALLOC. */
 sta_status sta_window_errors(const void *q, const void *k, const void *v, int batch, int heads, int T,
                              int H, int W, const int tile[3], int head_dim, float scale,
                              sta_dtype in_dtype, sta_layout layout, const int *candidates,

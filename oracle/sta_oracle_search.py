@@ -28,7 +28,9 @@ Parity pins (``tests/test_oracle_search_pins.py``): a window covering the
 grid has error exactly zero; a constant V makes every error zero (the
 cheapest window wins); attention confined to a query's own tile makes the
 1x1x1 window exact; the choice is checked against a brute-force scan of all
-candidates; planted mistakes must fail a pin.
+candidates; on a grid with partial tiles, the full window is exact and a
+candidate's error matches one computed against dense attention over the
+existing tokens; planted mistakes must fail a pin.
 """
 
 from __future__ import annotations
@@ -60,17 +62,20 @@ def odd_candidates(grid: Sequence[int]) -> list[tuple[int, int, int]]:
 
 
 def window_errors(q, k, v, video: Sequence[int], tile: Sequence[int], candidates,
-                  scale: float | None = None) -> np.ndarray:
+                  scale: float | None = None, partial: bool = False) -> np.ndarray:
     """err[h, c] = ||O_c - O_full|| / ||O_full|| for head h (reading W2).
 
     q, k, v: [B, heads, N, D] (natural order), any float dtype (widened to
-    float64).  Uses the explicit forward oracle; small inputs only."""
+    float64).  Uses the explicit forward oracle; small inputs only.
+    partial: extents need not be multiples of the tile (the forward
+    oracle's reading R11: ceil(extent / tile) tiles per axis, only existing
+    tokens take part); O_full is then attention over every existing token."""
     B, heads, N, D = q.shape
-    grid = F.tile_grid(video, tile)
-    full = F.sta_forward_explicit(q, k, v, video, tile, [grid] * heads, scale=scale)
+    grid = F.tile_grid(video, tile, partial)
+    full = F.sta_forward_explicit(q, k, v, video, tile, [grid] * heads, scale=scale, partial=partial)
     err = np.zeros((heads, len(candidates)))
     for c, w in enumerate(candidates):
-        o = F.sta_forward_explicit(q, k, v, video, tile, [tuple(w)] * heads, scale=scale)
+        o = F.sta_forward_explicit(q, k, v, video, tile, [tuple(w)] * heads, scale=scale, partial=partial)
         for h in range(heads):
             num = math.sqrt(float(((o[:, h] - full[:, h]) ** 2).sum()))
             den = math.sqrt(float((full[:, h] ** 2).sum()))
@@ -95,16 +100,17 @@ def select_windows(err: np.ndarray, candidates, grid: Sequence[int], threshold: 
 
 
 def search(samples, video: Sequence[int], tile: Sequence[int], candidates, threshold: float,
-           scale: float | None = None):
+           scale: float | None = None, partial: bool = False):
     """Readings W1-W4 over several calibration inputs: each sample's
     per-(head, candidate) errors (W1, W2), their arithmetic mean over the
     samples (W4), and the choice from the mean (W3).  samples: sequence of
-    (q, k, v), each [B, heads, N, D].  Returns (windows, mean errors)."""
-    errs = [window_errors(q, k, v, video, tile, candidates, scale=scale) for q, k, v in samples]
+    (q, k, v), each [B, heads, N, D].  partial: as in window_errors.
+    Returns (windows, mean errors)."""
+    errs = [window_errors(q, k, v, video, tile, candidates, scale=scale, partial=partial) for q, k, v in samples]
     if not errs:
         raise ValueError("no calibration samples")
     mean = np.zeros_like(errs[0])
     for e in errs:
         mean += e
     mean /= len(errs)
-    return select_windows(mean, candidates, F.tile_grid(video, tile), threshold), mean
+    return select_windows(mean, candidates, F.tile_grid(video, tile, partial), threshold), mean

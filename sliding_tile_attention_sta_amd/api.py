@@ -432,7 +432,7 @@ def window_search(samples, tile, threshold: float, candidates=None, scale: float
         _video_inputs(*s, None)
     q0, k0, v0 = samples[0]
     B, heads, T, H, W, D = _video_inputs(q0, k0, v0, None)
-    grid = tuple(e // t for e, t in zip((T, H, W), tile))
+    grid = tuple(-(-e // t) for e, t in zip((T, H, W), tile))   # partial tiles at the far edges count
     cands = [tuple(int(x) for x in w) for w in (candidates if candidates is not None else window_candidates(grid))]
     n = len(cands)
     if scale is None:

@@ -96,9 +96,13 @@ sta_status sta_window_errors(const void *q, const void *k, const void *v, int ba
   const int ext[3] = {T, H, W};
   for (int d = 0; d < 3; ++d)
     if (ext[d] < 1) return STA_ERR_ARG;
-  for (int d = 0; d < 3; ++d)
-    if (ext[d] % tile[d] != 0) return STA_ERR_SHAPE;
-  const int grid[3] = {T / tile[0], H / tile[1], W / tile[2]};
+  // Extents that are not multiples of the tile: plans with partial tiles
+  // (ceil(extent / tile) tiles per axis, only existing tokens take part).
+  bool partial = false;
+  for (int d = 0; d < 3; ++d) partial |= ext[d] % tile[d] != 0;
+  const int flags = partial ? STA_PLAN_PARTIAL_TILES : 0;
+  if (partial && layout != STA_LAYOUT_NATURAL) return STA_ERR_UNSUPPORTED;   // tile-major needs whole tiles
+  const int grid[3] = {(T + tile[0] - 1) / tile[0], (H + tile[1] - 1) / tile[1], (W + tile[2] - 1) / tile[2]};
   const int64_t plane = (int64_t)T * H * W * head_dim;
   const size_t out_bytes = (size_t)batch * heads * plane * sizeof(float);
   const size_t part_count = (size_t)batch * heads * sta::kRedBlocksPerPlane * 2;
@@ -117,7 +121,7 @@ sta_status sta_window_errors(const void *q, const void *k, const void *v, int ba
   for (int h = 0; h < heads; ++h)
     for (int d = 0; d < 3; ++d) win[h * 3 + d] = grid[d];
   sta::PlanHolder full;
-  sta_status st = sta_plan_create(batch, heads, T, H, W, tile, win.data(), head_dim, &full.p);
+  sta_status st = sta_plan_create_ex(batch, heads, T, H, W, tile, win.data(), head_dim, flags, &full.p);
   if (st != STA_OK) return st;
   int dev = -1;   // (after the argument checks, before any allocation on a device)
   if (hipGetDevice(&dev) != hipSuccess) return STA_ERR_HIP;
@@ -142,7 +146,7 @@ sta_status sta_window_errors(const void *q, const void *k, const void *v, int ba
   auto make = [&](int c, sta::PlanHolder &h) {
     for (int hh = 0; hh < heads; ++hh)
       for (int d = 0; d < 3; ++d) win[hh * 3 + d] = candidates[c * 3 + d];
-    return sta_plan_create(batch, heads, T, H, W, tile, win.data(), head_dim, &h.p);
+    return sta_plan_create_ex(batch, heads, T, H, W, tile, win.data(), head_dim, flags, &h.p);
   };
   st = make(0, cp[0]);
   if (st != STA_OK) return fail(st);
@@ -206,8 +210,8 @@ sta_status sta_window_search(const void *const *q, const void *const *k, const v
   for (double &x : mean) x /= n_samples;
   if (err_out)
     for (size_t j = 0; j < mean.size(); ++j) err_out[j] = mean[j];
-  // W3 on the mean (sta_window_errors checked that the extents are whole tiles)
-  const int grid[3] = {T / tile[0], H / tile[1], W / tile[2]};
+  // W3 on the mean, over the grid of (possibly partial) tiles
+  const int grid[3] = {(T + tile[0] - 1) / tile[0], (H + tile[1] - 1) / tile[1], (W + tile[2] - 1) / tile[2]};
   return sta_window_select(heads, grid, candidates, n_cand, mean.data(), threshold, window_out);
 }
 

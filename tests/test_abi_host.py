@@ -449,7 +449,9 @@ def test_window_search_argument_errors():
     t = _ints([2, 4, 4])
     c = _ints([1, 1, 1, 3, 3, 3])
     assert lib.sta_window_errors(None, P(1), P(2), 1, 2, 6, 16, 16, t, 64, 0.125, 0, 0, c, 2, err, None) == L.STA_ERR_ARG
-    assert lib.sta_window_errors(P(1), P(2), P(3), 1, 2, 7, 16, 16, t, 64, 0.125, 0, 0, c, 2, err, None) == L.STA_ERR_SHAPE
+    # extents that are not whole tiles: partial tiles, natural layout only
+    assert lib.sta_window_errors(P(1), P(2), P(3), 1, 2, 7, 16, 16, t, 64, 0.125, 0, L.STA_LAYOUT_TILE_MAJOR, c, 2,
+                                 err, None) == L.STA_ERR_UNSUPPORTED
     assert lib.sta_window_errors(P(1), P(2), P(3), 1, 2, 6, 16, 16, t, 64, 0.125, 0, 0, _ints([1, 0, 1]), 1, err, None) == L.STA_ERR_ARG
     assert lib.sta_window_errors(P(1), P(2), P(3), 1, 2, 6, 16, 16, t, 80, 0.125, 0, 0, c, 2, err, None) == L.STA_ERR_UNSUPPORTED
     out = _ints([0] * 6)

@@ -95,3 +95,34 @@ def test_window_search_averages_samples():
         # the library's mean is the mean of its own per-sample errors
         each = [api.window_errors(*(x.cuda() for x in s), TILE, cands) for s in samples]
         assert np.allclose(mean, (each[0] + each[1] + each[2]) / 3, rtol=1e-15, atol=0)
+
+
+def test_window_search_partial_tiles():
+    """Extents that are not multiples of the tile (5x15x13 with 2x4x4 tiles:
+    grid 3x4x4, the last tile of every axis partial): the errors and the
+    choice against the oracle with partial tiles; the grid candidate is
+    again exact."""
+    video = (5, 15, 13)
+    grid = (3, 4, 4)
+    say("case window search with partial tiles: 5x15x13 tile 2x4x4, 4 heads, d64 bf16")
+    q, k, v = make_local_qkv(video, LENGTHS, D, sharpness=16.0, seed=31)
+    cands = api.window_candidates(grid)
+    got = api.window_errors(q.cuda(), k.cuda(), v.cuda(), TILE, cands)
+    N = video[0] * video[1] * video[2]
+    ref_in = tuple(x.reshape(1, 4, N, D).double().numpy() for x in (q, k, v))
+    ref = OS.window_errors(*ref_in, video, TILE, cands, scale=1.0 / 8, partial=True)
+    d = np.abs(got - ref)
+    say(f"  max |err_gpu - err_oracle| {d.max():.2e}")
+    assert (d <= tol(ref)).all()
+    assert (got[:, cands.index(grid)] == 0).all()
+    tau = 0.1
+    windows, mean, got_cands = api.window_search([(q.cuda(), k.cuda(), v.cuda())], TILE, tau)
+    assert got_cands == [tuple(c) for c in cands]
+    want, _ = OS.search([ref_in], video, TILE, cands, tau, scale=1.0 / 8, partial=True)
+    say(f"  tau {tau}: {windows}")
+    for h in range(4):
+        if windows[h] == want[h]:
+            continue
+        lo, hi = ref[h] - tol(ref[h]), ref[h] + tol(ref[h])
+        assert windows[h] in (OS.select_windows(lo[None], cands, grid, tau)[0],
+                              OS.select_windows(hi[None], cands, grid, tau)[0]), (h, windows[h], want[h])

@@ -165,8 +165,39 @@ def pin_search_over_samples(mod, seed=6):
     return fails
 
 
+def pin_partial_grid(mod, seed=7):
+    # 5x7x3 with 2x3x2 tiles: grid (3, 3, 2), the last tile of every axis
+    # partial.  The grid window (and a wider one) is dense attention over the
+    # existing tokens, so its error is exactly zero; a candidate's error
+    # equals the one computed against torch's float64 dense attention (the
+    # forward oracle's partial tiles are pinned by brute force).
+    video, tile, grid = (5, 7, 3), (2, 3, 2), (3, 3, 2)
+    n = 5 * 7 * 3
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((1, 2, n, D)) for _ in range(3))
+    scale = 0.45
+    cands = [grid, (4, 5, 9), (1, 1, 1), (3, 1, 2), (1, 3, 1)]
+    err = mod.window_errors(q, k, v, video, tile, cands, scale=scale, partial=True)
+    dense = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x) for x in (q, k, v)), scale=scale).numpy()
+    fails = []
+    if not (err[:, :2] == 0).all():
+        fails.append(("full window error on a partial grid", err[:, :2].tolist()))
+    for c, w in enumerate(cands[2:], 2):
+        o = F.sta_forward_explicit(q, k, v, video, tile, [w] * 2, scale=scale, partial=True)
+        for h in range(2):
+            want = np.linalg.norm(o[:, h] - dense[:, h]) / np.linalg.norm(dense[:, h])
+            if not want > 0 or abs(err[h, c] - want) > 1e-12:
+                fails.append(("partial error", h, w, float(err[h, c]), float(want)))
+    windows, _ = mod.search([(q, k, v)], video, tile, cands[2:], -1.0, scale=scale, partial=True)
+    if windows != [grid] * 2:
+        fails.append(("fallback on a partial grid", windows))
+    return fails
+
+
 ALL_PINS = [pin_full_window_is_exact, pin_constant_v, pin_tile_confined_attention,
-            pin_error_against_dense_library, pin_choice_constraints, pin_search_over_samples]
+            pin_error_against_dense_library, pin_choice_constraints, pin_search_over_samples,
+            pin_partial_grid]
 
 
 def run_pins(mod):
@@ -203,8 +234,13 @@ MUTANTS = [
     ("sum of the samples, not their mean", "    mean /= len(errs)\n", "    pass\n"),
     ("last sample only", "        mean += e\n", "        mean = e.copy()\n"),
     ("dense reference with a 3-tile window",
-     "full = F.sta_forward_explicit(q, k, v, video, tile, [grid] * heads, scale=scale)",
-     "full = F.sta_forward_explicit(q, k, v, video, tile, [(3, 3, 3)] * heads, scale=scale)"),
+     "full = F.sta_forward_explicit(q, k, v, video, tile, [grid] * heads, scale=scale, partial=partial)",
+     "full = F.sta_forward_explicit(q, k, v, video, tile, [(3, 3, 3)] * heads, scale=scale, partial=partial)"),
+    ("partial tiles dropped from the grid", "grid = F.tile_grid(video, tile, partial)",
+     "grid = tuple(e // t for e, t in zip(video, tile))"),
+    ("partial flag not passed to the candidates",
+     "o = F.sta_forward_explicit(q, k, v, video, tile, [tuple(w)] * heads, scale=scale, partial=partial)",
+     "o = F.sta_forward_explicit(q, k, v, video, tile, [tuple(w)] * heads, scale=scale, partial=False)"),
 ]
 
 
