@@ -333,7 +333,9 @@ sta_status sta_backward_plan(const sta_plan *plan, const void *q, const void *k,
                              void *stream);
 
 /* Same, building (or finding in a process-wide cache keyed by every shape
- * and window argument) the plan itself.  Cached plans live until
+ * and window argument) the plan itself; extents that are not multiples of
+ * the tile get a plan with partial tiles (as STA_PLAN_PARTIAL_TILES of
+ * sta_plan_create_ex: natural layout only).  Cached plans live until
  * sta_clear_plan_cache or process exit.  Thread-safe: several threads may
  * call it at once, also while another clears the cache. */
 sta_status sta_forward(const void *q, const void *k, const void *v, void *out, int batch, int heads,

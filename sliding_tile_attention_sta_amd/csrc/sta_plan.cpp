@@ -567,7 +567,8 @@ std::shared_ptr<sta_plan> cached_plan(int batch, int heads, int T, int H, int W,
     auto it = g_cache.find(key);
     if (it != g_cache.end()) return it->second;
     sta_plan *p = nullptr;
-    *status = build_plan(batch, heads, T, H, W, tile, window, head_dim, false, &p);
+    // extents that are not multiples of the tile: a plan with partial tiles
+    *status = build_plan(batch, heads, T, H, W, tile, window, head_dim, true, &p);
     if (*status != STA_OK) return nullptr;
     // (if the shared state cannot be allocated, the constructor destroys p)
     std::shared_ptr<sta_plan> sp(p, [](sta_plan *x) { sta_plan_destroy(x); });

@@ -331,7 +331,9 @@ def test_forward_argument_errors_precede_device_work():
     assert lib.sta_tile_reorder(None, q, o, 0, None) == L.STA_ERR_ARG
     assert lib.sta_tile_unreorder(p.handle, q, o, 9, None) == L.STA_ERR_ARG
     t, win = _ints([2, 4, 4]), _ints([3, 3, 3, 3, 3, 3])
-    assert lib.sta_forward(q, k, v, o, 1, 2, 7, 16, 16, t, win, 64, 0.125, 0, 1, 0, None) == L.STA_ERR_SHAPE
+    # not whole tiles: a partial-tile plan, which takes the natural layout only
+    assert lib.sta_forward(q, k, v, o, 1, 2, 7, 16, 16, t, win, 64, 0.125, 0, 1, L.STA_LAYOUT_TILE_MAJOR,
+                           None) == L.STA_ERR_UNSUPPORTED
     assert lib.sta_forward(q, k, v, o, 1, 2, 6, 16, 16, t, win, 80, 0.125, 0, 1, 0, None) == L.STA_ERR_UNSUPPORTED
     assert lib.sta_forward(q, k, v, o, 1, 2, 6, 16, 16, None, win, 64, 0.125, 0, 1, 0, None) == L.STA_ERR_ARG
     assert lib.sta_clear_plan_cache() == L.STA_OK

@@ -195,3 +195,16 @@ def test_partial_autograd_function():
                                    w.tile, w.windows, scale=w.scale, partial=True)
     for nm, t in (("dq", qd.grad), ("dk", kd.grad), ("dv", vd.grad)):
         _check_grad(nm, t.reshape(shp).cpu().numpy(), ref[nm])
+
+
+def test_cached_entry_point_takes_partial_tiles():
+    """sta_forward (plan cache) on the exact 720p latent: the same result as
+    sta_forward_plan with a partial-tile plan, bit for bit."""
+    w = WORKLOADS["720p-exact"]
+    say(f"case {w.name}: sta_forward against sta_forward_plan")
+    q, k, v = (x.cuda() for x in make_qkv(w))
+    _, ref = _run(w, q, k, v)
+    got = api.sta_forward(q, k, v, w.tile, w.windows, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    api.sta_clear_plan_cache()
