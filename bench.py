@@ -633,6 +633,20 @@ def main():
                                    "sta_speedup": round(ms_d / ms, 2)}
         if w.dtype == "bf16":
             result["sdpa_dense_context"] = sdpa_dense(q, k, v, w.scale, stream, ms)
+        if w.name == "720p":
+            # the exact 720p latent (720 / 16 = 45 rows): partial tiles on H,
+            # the same number of tiles and the same work as the padded 48 rows
+            we = WORKLOADS["720p-exact"]
+            del dplan
+            qe, ke, ve = make_qkv(we, dev)
+            eplan = api.Plan(we.batch, we.heads, we.video, we.tile, we.windows, we.head_dim, partial_tiles=True)
+            oute = torch.empty(qe.shape, dtype=torch.float32, device=dev)
+            ms_e = timed(lambda: api.sta_forward_plan(eplan, qe, ke, ve, out=oute, scale=we.scale,
+                                                      stream=stream), max(3, args.steps // 2), 3, stream)
+            result["exact_latent"] = {"video": list(we.video), "ms": round(ms_e, 4),
+                                      "tflops_whole_tiles": round(eplan.flops / (ms_e * 1e-3) / 1e12, 2),
+                                      "vs_padded": round(ms_e / ms, 3)}
+            del qe, ke, ve, oute, eplan
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v)
