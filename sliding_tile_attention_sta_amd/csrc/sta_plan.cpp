@@ -55,8 +55,31 @@ std::vector<std::vector<int32_t>> build_queues(const sta_plan *p, const std::vec
     int h = (int)((rest / p->n_tiles) % p->heads);
     return (int64_t)off[(size_t)h * p->n_tiles + t + 1] - off[(size_t)h * p->n_tiles + t];
   };
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int64_t a, int64_t b) { return cost(a) > cost(b); });
+  // ties: by (batch, head), then the tile's Morton (Z-order) code, so that
+  // a chunk of consecutive items (the ones an XCD runs at once) is a compact
+  // block of tiles whose windows overlap, and the work groups of an XCD
+  // read the same key/value blocks from its L2 at about the same step
+  // (a raster run of 32 tiles spans twice the key tiles of a 2x4x4 block)
+  const int nH = p->grid[1], nW = p->grid[2];
+  auto morton = [&](int t) {
+    const uint32_t c[3] = {(uint32_t)(t / (nH * nW)), (uint32_t)((t / nW) % nH), (uint32_t)(t % nW)};
+    uint64_t m = 0;
+    for (int b = 0; b < 16; ++b)
+      for (int d = 0; d < 3; ++d) m |= (uint64_t)((c[d] >> b) & 1u) << (3 * b + (2 - d));
+    return m;
+  };
+  std::vector<uint64_t> mk((size_t)p->n_tiles);
+  for (int t = 0; t < p->n_tiles; ++t) mk[t] = morton(t);
+  std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
+    const int64_t ca = cost(a), cb = cost(b);
+    if (ca != cb) return ca > cb;
+    const int64_t ra = a / subs, rb = b / subs;
+    const int64_t ga = ra / p->n_tiles, gb = rb / p->n_tiles;
+    if (ga != gb) return ga < gb;
+    const uint64_t ma = mk[ra % p->n_tiles], mb = mk[rb % p->n_tiles];
+    if (ma != mb) return ma < mb;
+    return a < b;
+  });
   if (n_whole < 0) n_whole = n_items;
   const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(kCusPerXcd, (n_whole + kXcds - 1) / kXcds));
   std::vector<std::vector<int32_t>> queue(kXcds);
